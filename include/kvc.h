@@ -1,0 +1,232 @@
+/*
+ * kvc.h - paged sliding-window KV cache and paged attention for MI355X (gfx950).
+ *
+ * C ABI of libkvc.so.  Plain pointers and sizes only; no C++ or framework
+ * types cross this boundary.
+ *
+ * What the library computes
+ *   A per-layer KV cache cut into fixed-size pages that are kept in three
+ *   streams ("LingBot-Map Paged KV Cache", section 2): scale pages that are
+ *   never evicted, sliding-window patch pages that return to a free list once
+ *   outside the window and are reused by the next unit, and append-only
+ *   special pages packing the special tokens of many frames (42 frames of 6
+ *   tokens per 256-slot page).  The visible page table lists scale, then
+ *   window, then special pages; each page carries its valid length, so the
+ *   partly filled last page needs no mask.  A non-keyframe is appended,
+ *   attended and rolled back (section 3).  The same cache runs the chunked
+ *   form of "vLLM-Omni RFC #2727: Reconstruction Engine" (section 1 and 2.3):
+ *   a unit is a chunk of frames, the window holds the most recent
+ *   sliding_window_num chunks including the current one; an unbounded window
+ *   is full global attention and a window of 1 gives independent chunks.
+ *   paged_attn_fwd computes softmax attention of query tokens against the
+ *   tokens of a page table (no mask), with an online softmax over pages.
+ *
+ * Allocation policy (fixed so that tables are reproducible):
+ *   - free list is a LIFO stack; a fresh cache pops pages 0, 1, 2, ...
+ *   - an append pops the unit's patch pages, then (when needed) one special
+ *     page; after the pops, the oldest window unit is evicted if the window
+ *     holds more than window_units units; evicted pages are pushed in
+ *     reverse, so a later pop returns the unit's first page first.
+ *   - the first num_scale_units units go to the scale stream, later ones to
+ *     the window; every unit's special tokens go to the special stream.
+ *   - rollback undoes the last append exactly (single level).
+ *
+ * Device memory
+ *   The caller owns all device memory (pools, Q/K/V/O, tables, workspace).
+ *   The library owns host metadata only and allocates no device memory.
+ *   Pool layout for a cache with H heads, head_dim d, page size P:
+ *     K pool: [num_pages][H][P][d]   (slot-major rows of d elements)
+ *     V pool: [num_pages][H][d][P]   (transposed: one row of P slots per dim)
+ *   Element type is bf16 (2 bytes) or fp32 (4 bytes), per kvc_config.dtype.
+ *   K/V/Q/O activations are [tokens][H][d], tokens in order.
+ *
+ * Streams and threads
+ *   Device work is enqueued on the hipStream_t passed in (0 = null stream)
+ *   and is asynchronous to the host.  A handle is not thread-safe; use one
+ *   stream for every call on a handle, so that an append that recycles a page
+ *   is ordered after earlier attention reads of it.
+ *
+ * Errors
+ *   Every call returns KVC_OK (0) or a negative kvc_status.  On error the
+ *   handle's state is unchanged.  kvc_last_error() gives a thread-local
+ *   message for the last failing call on the calling thread.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* kvc_stream_t; /* same type as hipStream_t */
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARGUMENT = -1,
+  KVC_ERR_OUT_OF_PAGES = -2,
+  KVC_ERR_NO_UNDO = -3,
+  KVC_ERR_BUFFER_TOO_SMALL = -4,
+  KVC_ERR_UNSUPPORTED = -5,
+  KVC_ERR_DEVICE = -6,
+} kvc_status;
+
+typedef enum kvc_dtype { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F32 = 1 } kvc_dtype;
+
+typedef enum kvc_special_packing {
+  /* floor(P / special_tokens) whole frames per special page (42 for 6 tokens
+   * in 256 slots); a frame never straddles two pages. */
+  KVC_SPECIAL_FRAME_ALIGNED = 0,
+  /* special tokens packed back to back; a frame may straddle two pages. */
+  KVC_SPECIAL_CONTIGUOUS = 1,
+} kvc_special_packing;
+
+typedef struct kvc_config {
+  int32_t num_heads;        /* H >= 1 */
+  int32_t head_dim;         /* d; device paths need 64 */
+  int32_t page_size;        /* P tokens per page; device paths need a multiple of 64 */
+  int32_t dtype;            /* kvc_dtype */
+  int32_t patch_tokens;     /* tokens per unit in the patch stream (frame 256, VGGT frame 1374, chunk 8*1374) */
+  int32_t special_tokens;   /* special tokens per unit, 0 <= X <= P (6 for LingBot-Map frames) */
+  int32_t num_scale_units;  /* S: first S units are never evicted */
+  int32_t window_units;     /* W: window size in units including the newest; <= 0 = unbounded */
+  int32_t special_packing;  /* kvc_special_packing */
+  int32_t max_units;        /* most units ever cached at once (sizes the special stream) */
+  int32_t num_pages;        /* pool capacity in pages; 0 = kvc_required_pages */
+} kvc_config;
+
+/* Snapshot of the host metadata.  The caller provides the arrays, each with
+ * room for `capacity` entries (num_pages is always enough).  Page lists are
+ * in table order; free_pages runs from the bottom of the stack to the top
+ * (the next page popped is free_pages[num_free - 1]). */
+typedef struct kvc_state {
+  int32_t capacity;
+  int32_t* free_pages;
+  int32_t* scale_pages;
+  int32_t* window_pages;
+  int32_t* special_pages;
+  int32_t num_free;
+  int32_t num_scale_pages;
+  int32_t num_window_pages;
+  int32_t num_window_units;
+  int32_t num_special_pages;
+  int32_t special_fill;     /* frames (frame-aligned) or tokens (contiguous) in the last special page */
+  int32_t num_units;        /* units currently cached */
+  int32_t has_undo;         /* 1 if kvc_rollback_last_frame would succeed */
+  int32_t num_pages;        /* pool capacity */
+} kvc_state;
+
+typedef struct kvc_cache kvc_t;
+
+/* Pages a cache with this config needs: with a bounded window,
+ * min(max_units, S + W + 1) units of ceil(patch_tokens / P) pages (one unit
+ * more than the window holds, since an append pops before it evicts), plus the
+ * special pages of max_units units; with an unbounded window, max_units units. */
+int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages);
+
+/* Bytes of one pool (K or V): num_pages * H * P * d * sizeof(element). */
+int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes);
+
+/* Create a cache.  k_pool / v_pool: caller-owned device buffers of
+ * kvc_pool_bytes each (layouts above), or both NULL for a host-only handle
+ * that tracks metadata without device work (appends then take NULL K/V).
+ * The pools are not cleared.  *out receives the handle. */
+int kvc_create(const kvc_config* cfg, void* k_pool, void* v_pool, kvc_t** out);
+int kvc_destroy(kvc_t* cache);
+
+/* Append one unit ("LingBot-Map Paged KV Cache", section 2; RFC #2727,
+ * section 3.3: KV append, then eviction of the oldest chunk beyond the
+ * window).  k_unit / v_unit: device [patch_tokens + special_tokens][H][d],
+ * patch tokens first, in the cache dtype; both NULL on a host-only handle.
+ * Plans on the host and enqueues one scatter kernel on `stream`.
+ * KVC_ERR_OUT_OF_PAGES when the free list cannot supply the unit. */
+int kvc_append_frame(kvc_t* cache, const void* k_unit, const void* v_unit, kvc_stream_t stream);
+
+/* Undo the last append exactly ("LingBot-Map Paged KV Cache", section 3: a
+ * non-keyframe is appended, attended, then rolled back).  Host-only: evicted
+ * pages were never overwritten, so no device work is needed.  Single level;
+ * KVC_ERR_NO_UNDO if there is nothing to undo. */
+int kvc_rollback_last_frame(kvc_t* cache);
+
+/* Drop every unit and restore the fresh free-list order. */
+int kvc_reset(kvc_t* cache);
+
+/* Visible page table ("LingBot-Map Paged KV Cache", section 2): scale pages
+ * (oldest first), window pages (oldest unit first), special pages (in the
+ * order they were opened).  page_ids / page_lens: host arrays of `capacity`
+ * entries; page_lens[i] is the number of valid tokens in page i (P except a
+ * unit's last page, full frame-aligned special pages and the last special
+ * page).  *num_pages receives the count (also on KVC_ERR_BUFFER_TOO_SMALL);
+ * *last_page_len receives page_lens[num_pages - 1] (0 when empty).  Either
+ * output pointer except num_pages may be NULL. */
+int kvc_build_visible_table(const kvc_t* cache, int32_t* page_ids, int32_t* page_lens,
+                            int32_t capacity, int32_t* num_pages, int32_t* last_page_len);
+
+/* Copy of the metadata; see kvc_state. */
+int kvc_get_state(const kvc_t* cache, kvc_state* out);
+
+/* ------------------------------------------------------------------------ */
+/* Paged attention                                                            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct paged_attn_args {
+  int32_t dtype;            /* kvc_dtype of q, pools and o */
+  int32_t num_heads;        /* H */
+  int32_t head_dim;         /* d = 64 */
+  int32_t page_size;        /* P, multiple of 64 */
+  float sm_scale;           /* score scale; 1/sqrt(d) is the usual value */
+  int32_t num_seqs;         /* independent query sequences in this call */
+  int32_t total_q;          /* rows of q and o */
+  int32_t max_qo_len;       /* host-known max over sequences of query rows */
+  int32_t max_kv_pages;     /* host-known max over sequences of table entries */
+  int32_t num_pool_pages;   /* pool capacity; table ids outside [0, num_pool_pages) are skipped */
+  int32_t num_splits;       /* key-range splits per sequence: 0 = library's choice, 1 = none */
+  const int32_t* qo_indptr; /* device [num_seqs + 1]: sequence s owns q rows [qo_indptr[s], qo_indptr[s+1]) */
+  const int32_t* kv_indptr; /* device [num_seqs + 1]: and table entries [kv_indptr[s], kv_indptr[s+1]) */
+  const int32_t* page_ids;  /* device table: page id per entry */
+  const int32_t* page_lens; /* device table: valid tokens per entry, clamped to [0, P] */
+  const void* q;            /* device [total_q][H][d] */
+  const void* k_pool;       /* device K pool (layout above) */
+  const void* v_pool;       /* device V pool (layout above) */
+  void* o;                  /* device [total_q][H][d]; rows of a sequence with no keys are 0 */
+  float* lse;               /* device [total_q][H] natural-log sum of exp of scaled scores, or NULL */
+  void* workspace;          /* device scratch of paged_attn_workspace_size bytes (NULL if 0) */
+  size_t workspace_bytes;
+} paged_attn_args;
+
+/* Workspace bytes paged_attn_fwd needs for these arguments (split-key
+ * partial outputs and log-sum-exps).  Reads only host fields of args. */
+int paged_attn_workspace_size(const paged_attn_args* args, size_t* bytes);
+
+/* Split count paged_attn_fwd will use for these arguments. */
+int paged_attn_num_splits(const paged_attn_args* args, int32_t* num_splits);
+
+/* O = softmax(sm_scale * Q K^T) V per sequence and head over the tokens of
+ * the sequence's table entries, no mask ("LingBot-Map Paged KV Cache",
+ * sections 1-2; RFC #2727, section 1).  bf16: matrix-core products with fp32
+ * accumulation and an fp32 online softmax; fp32: fp32 throughout.  Enqueued
+ * on `stream`; KVC_ERR_UNSUPPORTED for shapes the kernels do not cover. */
+int paged_attn_fwd(const paged_attn_args* args, kvc_stream_t stream);
+
+/* Merge split partials: part i of row r, head h holds a normalised output
+ * O_i and its log-sum-exp lse_i; writes O = sum_i exp(lse_i - lse) O_i with
+ * lse = log sum_i exp(lse_i).  partial_o: device fp32 [num_parts][rows][H][d],
+ * partial_lse: device fp32 [num_parts][rows][H]; o in `dtype`, lse nullable.
+ * Exposed for testing the merge on its own; paged_attn_fwd calls it when it
+ * splits. */
+int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
+                     const float* partial_o, const float* partial_lse, void* o, float* lse,
+                     kvc_stream_t stream);
+
+const char* kvc_strerror(int status);
+const char* kvc_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

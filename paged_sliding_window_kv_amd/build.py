@@ -1,0 +1,84 @@
+"""Build libkvc.so in-tree for gfx950 with hipcc.
+
+    python -m paged_sliding_window_kv_amd.build          # build (always recompiles)
+    python -m paged_sliding_window_kv_amd.build --debug  # -O1 -g host code
+
+Objects go to paged_sliding_window_kv_amd/_build/, the library to
+paged_sliding_window_kv_amd/libkvc.so.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libkvc.so")
+ARCH = os.environ.get("KVC_OFFLOAD_ARCH", "gfx950")
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def common_flags(debug: bool):
+    opt = ["-O1", "-g"] if debug else ["-O3"]
+    return opt + ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def compile_one(src: str, debug: bool) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if src.endswith(".hip") or os.path.basename(src) == "api.cpp":
+        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-x", "hip", src, "-c", "-o", obj,
+               # packed fp32 VALU forms are kept out of the generated code
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + common_flags(debug)
+    else:
+        cmd = ["g++", src, "-c", "-o", obj] + common_flags(debug)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+    return obj
+
+
+def build(debug: bool = False, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: compile_one(s, debug), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--debug", action="store_true")
+    a = ap.parse_args()
+    build(debug=a.debug)
+
+
+if __name__ == "__main__":
+    main()

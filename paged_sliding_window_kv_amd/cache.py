@@ -1,0 +1,167 @@
+"""Python handle over one layer's paged KV cache (libkvc.so).
+
+Marshalling only: page planning, the visible table and rollback run in the
+library's C++ host code, the K/V scatter and the attention in its HIP
+kernels.  PyTorch provides the device memory (the two pools) and the stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import _lib as L
+
+_DTYPES = {"bf16": L.KVC_DTYPE_BF16, "f32": L.KVC_DTYPE_F32}
+_PACKING = {"frame_aligned": L.KVC_SPECIAL_FRAME_ALIGNED, "contiguous": L.KVC_SPECIAL_CONTIGUOUS}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(dtype: str):
+    t = _torch()
+    return {"bf16": t.bfloat16, "f32": t.float32}[dtype]
+
+
+def current_stream_ptr(device=None) -> int:
+    t = _torch()
+    return t.cuda.current_stream(device).cuda_stream
+
+
+class KvCache:
+    """One layer's cache.
+
+    device=None gives a host-only handle: appends take no data and only the
+    page metadata moves (useful to check tables without a GPU).  Otherwise the
+    K pool [num_pages, H, P, d] and the V pool [num_pages, H, d, P] are
+    allocated on `device` and appends scatter device K/V into them.
+    """
+
+    def __init__(self, num_heads: int, head_dim: int = 64, page_size: int = 256, dtype: str = "bf16",
+                 patch_tokens: int = 256, special_tokens: int = 6, num_scale_units: int = 8,
+                 window_units: int = 64, special_packing: str = "frame_aligned", max_units: int = 1000,
+                 num_pages: int = 0, device=None):
+        self.cfg = L.KvcConfig(num_heads, head_dim, page_size, _DTYPES[dtype], patch_tokens, special_tokens,
+                               num_scale_units, window_units, _PACKING[special_packing], max_units, num_pages)
+        self.dtype = dtype
+        self.num_heads, self.head_dim, self.page_size = num_heads, head_dim, page_size
+        self.patch_tokens, self.special_tokens = patch_tokens, special_tokens
+        self.unit_tokens = patch_tokens + special_tokens
+        lib = L.lib()
+        n = C.c_int32(num_pages)
+        if num_pages == 0:
+            L.check(lib.kvc_required_pages(C.byref(self.cfg), C.byref(n)), "kvc_required_pages")
+        self.num_pages = n.value
+        self.device = device
+        self.k_pool = self.v_pool = None
+        if device is not None:
+            t = _torch()
+            td = torch_dtype(dtype)
+            self.k_pool = t.empty((self.num_pages, num_heads, page_size, head_dim), dtype=td, device=device)
+            self.v_pool = t.empty((self.num_pages, num_heads, head_dim, page_size), dtype=td, device=device)
+        h = C.c_void_p()
+        L.check(lib.kvc_create(C.byref(self.cfg), self._ptr(self.k_pool), self._ptr(self.v_pool), C.byref(h)),
+                "kvc_create")
+        self._h = h
+        self._ids = np.zeros(self.num_pages, np.int32)
+        self._lens = np.zeros(self.num_pages, np.int32)
+
+    @staticmethod
+    def _ptr(t) -> Optional[int]:
+        return None if t is None else t.data_ptr()
+
+    @property
+    def handle(self) -> C.c_void_p:
+        return self._h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            L.lib().kvc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- stream operations ------------------------------------------------------
+    def append(self, k=None, v=None, stream: Optional[int] = None) -> None:
+        """Append one unit.  k, v: [patch + special, H, d] device tensors in the cache dtype."""
+        if self.device is None:
+            if k is not None or v is not None:
+                raise ValueError("host-only cache takes no K/V")
+            L.check(L.lib().kvc_append_frame(self._h, None, None, None), "kvc_append_frame")
+            return
+        self._check_unit(k, "k")
+        self._check_unit(v, "v")
+        s = current_stream_ptr(k.device) if stream is None else stream
+        L.check(L.lib().kvc_append_frame(self._h, k.data_ptr(), v.data_ptr(), s), "kvc_append_frame")
+
+    def _check_unit(self, x, name):
+        t = _torch()
+        want = (self.unit_tokens, self.num_heads, self.head_dim)
+        if not isinstance(x, t.Tensor) or tuple(x.shape) != want:
+            raise ValueError(f"{name} must be a tensor of shape {want}")
+        if x.dtype != torch_dtype(self.dtype) or not x.is_contiguous() or x.device != self.k_pool.device:
+            raise ValueError(f"{name} must be a contiguous {self.dtype} tensor on {self.k_pool.device}")
+
+    def rollback(self) -> None:
+        L.check(L.lib().kvc_rollback_last_frame(self._h), "kvc_rollback_last_frame")
+
+    def reset(self) -> None:
+        L.check(L.lib().kvc_reset(self._h), "kvc_reset")
+
+    # -- metadata -----------------------------------------------------------------
+    def visible_table(self) -> Tuple[np.ndarray, np.ndarray]:
+        n = C.c_int32()
+        last = C.c_int32()
+        ip = self._ids.ctypes.data_as(C.POINTER(C.c_int32))
+        lp = self._lens.ctypes.data_as(C.POINTER(C.c_int32))
+        L.check(L.lib().kvc_build_visible_table(self._h, ip, lp, self.num_pages, C.byref(n), C.byref(last)),
+                "kvc_build_visible_table")
+        return self._ids[:n.value].copy(), self._lens[:n.value].copy()
+
+    def state(self) -> dict:
+        cap = self.num_pages
+        bufs = [np.zeros(cap, np.int32) for _ in range(4)]
+        st = L.KvcState()
+        st.capacity = cap
+        st.free_pages, st.scale_pages, st.window_pages, st.special_pages = (
+            b.ctypes.data_as(C.POINTER(C.c_int32)) for b in bufs)
+        L.check(L.lib().kvc_get_state(self._h, C.byref(st)), "kvc_get_state")
+        return {
+            "free": bufs[0][:st.num_free].tolist(),
+            "scale_pages": bufs[1][:st.num_scale_pages].tolist(),
+            "window_pages": bufs[2][:st.num_window_pages].tolist(),
+            "window_units": st.num_window_units,
+            "special_pages": bufs[3][:st.num_special_pages].tolist(),
+            "special_fill": st.special_fill,
+            "num_units": st.num_units,
+            "has_undo": bool(st.has_undo),
+        }
+
+    # -- attention ------------------------------------------------------------------
+    def attend(self, q, out=None, lse=None, sm_scale: Optional[float] = None, num_splits: int = 0,
+               stream: Optional[int] = None):
+        """Attention of q [Lq, H, d] against the visible table (one sequence).
+
+        The table is built on the host and copied to the device for the call.
+        Returns (out, lse).
+        """
+        from .attention import paged_attention
+        t = _torch()
+        ids, lens = self.visible_table()
+        dev = self.k_pool.device
+        page_ids = t.from_numpy(ids).to(dev)
+        page_lens = t.from_numpy(lens).to(dev)
+        qo = t.tensor([0, q.shape[0]], dtype=t.int32, device=dev)
+        kv = t.tensor([0, len(ids)], dtype=t.int32, device=dev)
+        return paged_attention(q, self.k_pool, self.v_pool, page_ids, page_lens, qo, kv,
+                               max_qo_len=q.shape[0], max_kv_pages=len(ids), out=out, lse=lse,
+                               sm_scale=sm_scale, num_splits=num_splits, stream=stream)

@@ -1,0 +1,314 @@
+// C ABI of libkvc.so (declared in include/kvc.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "kvc.h"
+#include "page_cache.hpp"
+
+struct kvc_cache {
+  kvc::PageCache pc;
+  void* k_pool;
+  void* v_pool;
+  explicit kvc_cache(const kvc_config& c) : pc(c), k_pool(nullptr), v_pool(nullptr) {}
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+size_t elem_size(int dtype) { return dtype == KVC_DTYPE_BF16 ? 2 : 4; }
+
+bool device_shapes_ok(const kvc_config& c) {
+  return c.head_dim == kvc::kHeadDim && c.page_size % kvc::kKeyTile == 0;
+}
+
+constexpr int kXcds = 8;
+
+int choose_waves(const paged_attn_args& a) {
+  // 8 waves (256 query rows) once there are enough rows to fill them.
+  return a.max_qo_len >= 1024 ? 8 : 4;
+}
+
+int rows_per_tile(const paged_attn_args& a) {
+  return a.dtype == KVC_DTYPE_BF16 ? kvc::attn_bf16_rows_per_tile(choose_waves(a)) : kvc::attn_f32_rows_per_tile();
+}
+
+int choose_splits(const paged_attn_args& a) {
+  if (a.num_splits > 0) return std::max(1, std::min(a.num_splits, std::max(1, a.max_kv_pages)));
+  if (a.max_kv_pages <= 1) return 1;
+  const int rows = rows_per_tile(a);
+  const long tiles = static_cast<long>((a.max_qo_len + rows - 1) / rows) * a.num_seqs * a.num_heads;
+  // Aim for about two workgroups per compute unit (256 CUs), keeping at least
+  // two pages per split so the merge traffic stays small against K/V reads.
+  const long target = 512;
+  if (tiles >= target) return 1;
+  long s = (target + tiles - 1) / tiles;
+  s = std::min<long>(s, std::max(1, a.max_kv_pages / 2));
+  return static_cast<int>(std::max<long>(1, std::min<long>(s, 64)));
+}
+
+int check_attn_args(const paged_attn_args* a) {
+  if (!a) return fail(KVC_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->dtype != KVC_DTYPE_BF16 && a->dtype != KVC_DTYPE_F32)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "bad dtype %d", a->dtype);
+  if (a->head_dim != kvc::kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "head_dim %d (kernels need 64)", a->head_dim);
+  if (a->page_size <= 0 || a->page_size % kvc::kKeyTile != 0)
+    return fail(KVC_ERR_UNSUPPORTED, "page_size %d (kernels need a multiple of 64)", a->page_size);
+  if (a->num_heads <= 0 || a->num_seqs < 0 || a->total_q < 0 || a->max_qo_len < 0 || a->max_kv_pages < 0 ||
+      a->num_pool_pages < 0 || a->num_splits < 0)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "negative size in paged_attn_args");
+  if (!(std::isfinite(a->sm_scale) && a->sm_scale > 0.f))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+  return KVC_OK;
+}
+
+size_t workspace_for(const paged_attn_args& a, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rh = static_cast<size_t>(a.total_q) * a.num_heads;
+  const size_t o = static_cast<size_t>(splits) * rh * kvc::kHeadDim * sizeof(float);
+  const size_t l = static_cast<size_t>(splits) * rh * sizeof(float);
+  return ((o + 255) & ~size_t(255)) + l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_strerror(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KVC_ERR_OUT_OF_PAGES: return "out of pages";
+    case KVC_ERR_NO_UNDO: return "no append to roll back";
+    case KVC_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case KVC_ERR_UNSUPPORTED: return "unsupported";
+    case KVC_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+int kvc_version(void) { return 100; }
+
+int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages) {
+  if (!cfg || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+  const int32_t n = kvc::PageCache::required_pages(*cfg);
+  if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+  *num_pages = n;
+  return KVC_OK;
+}
+
+int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes) {
+  if (!cfg || !bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+  const int32_t n = cfg->num_pages > 0 ? cfg->num_pages : kvc::PageCache::required_pages(*cfg);
+  if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+  *bytes = static_cast<size_t>(n) * cfg->num_heads * cfg->page_size * cfg->head_dim * elem_size(cfg->dtype);
+  return KVC_OK;
+}
+
+int kvc_create(const kvc_config* cfg, void* k_pool, void* v_pool, kvc_t** out) {
+  if (!cfg || !out) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+  if ((k_pool == nullptr) != (v_pool == nullptr))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must both be set or both be NULL");
+  if (k_pool && !device_shapes_ok(*cfg))
+    return fail(KVC_ERR_UNSUPPORTED, "device pools need head_dim 64 and page_size a multiple of 64");
+  const int64_t u = (int64_t(cfg->patch_tokens) + cfg->page_size - 1) / cfg->page_size;
+  if (k_pool && u > kvc::kMaxUnitPages)
+    return fail(KVC_ERR_UNSUPPORTED, "a unit spans %lld pages (max %d)", static_cast<long long>(u),
+                kvc::kMaxUnitPages);
+  if (kvc::PageCache::required_pages(*cfg) < 0 && cfg->num_pages == 0)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+  kvc_cache* c = new (std::nothrow) kvc_cache(*cfg);
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "out of host memory");
+  c->k_pool = k_pool;
+  c->v_pool = v_pool;
+  *out = c;
+  return KVC_OK;
+}
+
+int kvc_destroy(kvc_t* cache) {
+  delete cache;
+  return KVC_OK;
+}
+
+int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  const bool device = c->k_pool != nullptr;
+  if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
+  if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
+  kvc::AppendPlan plan;
+  const int s = c->pc.append(device ? &plan : nullptr);
+  if (s != KVC_OK) return fail(s, "append needs %d pages", c->pc.unit_pages());
+  if (!device) return KVC_OK;
+  const kvc_config& cfg = c->pc.config();
+  kvc::AppendParams p{};
+  p.k_src = k_unit;
+  p.v_src = v_unit;
+  p.k_pool = c->k_pool;
+  p.v_pool = c->v_pool;
+  p.num_heads = cfg.num_heads;
+  p.page_size = cfg.page_size;
+  p.patch_tokens = cfg.patch_tokens;
+  p.special_tokens = cfg.special_tokens;
+  p.special_page0 = plan.special_page0;
+  p.special_slot0 = plan.special_slot0;
+  p.special_count0 = plan.special_count0;
+  p.special_page1 = plan.special_page1;
+  p.num_unit_pages = static_cast<int32_t>(plan.unit_pages.size());
+  std::copy(plan.unit_pages.begin(), plan.unit_pages.end(), p.unit_pages);
+  const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    c->pc.rollback();  // keep the strong guarantee
+    return fail(KVC_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  }
+  return KVC_OK;
+}
+
+int kvc_rollback_last_frame(kvc_t* c) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  const int s = c->pc.rollback();
+  return s == KVC_OK ? KVC_OK : fail(s, "nothing to roll back");
+}
+
+int kvc_reset(kvc_t* c) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  c->pc.reset();
+  return KVC_OK;
+}
+
+int kvc_build_visible_table(const kvc_t* c, int32_t* page_ids, int32_t* page_lens, int32_t capacity,
+                            int32_t* num_pages, int32_t* last_page_len) {
+  if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  const int32_t n = c->pc.visible_count();
+  *num_pages = n;
+  if ((page_ids || page_lens) && capacity < n)
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "table needs %d entries, capacity %d", n, capacity);
+  if (page_ids && page_lens) {
+    c->pc.visible_table(page_ids, page_lens);
+    if (last_page_len) *last_page_len = n ? page_lens[n - 1] : 0;
+    return KVC_OK;
+  }
+  std::vector<int32_t> ids(n), lens(n);
+  c->pc.visible_table(ids.data(), lens.data());
+  if (page_ids) std::copy(ids.begin(), ids.end(), page_ids);
+  if (page_lens) std::copy(lens.begin(), lens.end(), page_lens);
+  if (last_page_len) *last_page_len = n ? lens[n - 1] : 0;
+  return KVC_OK;
+}
+
+int kvc_get_state(const kvc_t* c, kvc_state* st) {
+  if (!c || !st) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (st->capacity < c->pc.num_pages() &&
+      (st->free_pages || st->scale_pages || st->window_pages || st->special_pages))
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "state arrays need %d entries", c->pc.num_pages());
+  c->pc.state(st);
+  return KVC_OK;
+}
+
+int paged_attn_workspace_size(const paged_attn_args* a, size_t* bytes) {
+  if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
+  if (int s = check_attn_args(a)) return s;
+  *bytes = workspace_for(*a, choose_splits(*a));
+  return KVC_OK;
+}
+
+int paged_attn_num_splits(const paged_attn_args* a, int32_t* num_splits) {
+  if (!num_splits) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL num_splits");
+  if (int s = check_attn_args(a)) return s;
+  *num_splits = choose_splits(*a);
+  return KVC_OK;
+}
+
+int paged_attn_fwd(const paged_attn_args* a, kvc_stream_t stream) {
+  if (int s = check_attn_args(a)) return s;
+  if (a->num_seqs == 0 || a->total_q == 0 || a->max_qo_len == 0) return KVC_OK;
+  if (!a->qo_indptr || !a->kv_indptr || !a->q || !a->o)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (a->max_kv_pages > 0 && (!a->page_ids || !a->page_lens || !a->k_pool || !a->v_pool))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "NULL table or pool pointer");
+  const int splits = choose_splits(*a);
+  const size_t need = workspace_for(*a, splits);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes", need);
+  const int rows = rows_per_tile(*a);
+  const long q_tiles = (a->max_qo_len + rows - 1) / rows;
+  const long groups = static_cast<long>(a->num_seqs) * a->num_heads * splits;
+  const long groups_padded = (groups + kXcds - 1) / kXcds * kXcds;
+  if (q_tiles * groups_padded > 0x7fffffffL) return fail(KVC_ERR_UNSUPPORTED, "grid too large");
+
+  kvc::AttnParams p{};
+  p.q = a->q;
+  p.k_pool = a->k_pool;
+  p.v_pool = a->v_pool;
+  p.o = a->o;
+  p.lse = a->lse;
+  if (splits > 1) {
+    const size_t rh = static_cast<size_t>(a->total_q) * a->num_heads;
+    p.part_o = static_cast<float*>(a->workspace);
+    const size_t obytes = (static_cast<size_t>(splits) * rh * kvc::kHeadDim * sizeof(float) + 255) & ~size_t(255);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + obytes);
+  }
+  p.qo_indptr = a->qo_indptr;
+  p.kv_indptr = a->kv_indptr;
+  p.page_ids = a->page_ids;
+  p.page_lens = a->page_lens;
+  p.num_heads = a->num_heads;
+  p.page_size = a->page_size;
+  p.num_pool_pages = a->num_pool_pages;
+  p.num_seqs = a->num_seqs;
+  p.total_q = a->total_q;
+  p.q_tiles = static_cast<int32_t>(q_tiles);
+  p.num_splits = splits;
+  p.groups = static_cast<int32_t>(groups);
+  p.groups_padded = static_cast<int32_t>(groups_padded);
+  p.sm_scale = a->sm_scale;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = a->dtype == KVC_DTYPE_BF16 ? kvc::launch_attn_bf16(p, choose_waves(*a), st)
+                                            : kvc::launch_attn_f32(p, st);
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
+  if (splits > 1) {
+    e = kvc::launch_attn_merge(a->dtype, splits, a->total_q, a->num_heads, p.part_o, p.part_lse, a->o, a->lse, st);
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  }
+  return KVC_OK;
+}
+
+int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
+                     const float* partial_o, const float* partial_lse, void* o, float* lse, kvc_stream_t stream) {
+  if (dtype != KVC_DTYPE_BF16 && dtype != KVC_DTYPE_F32) return fail(KVC_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (head_dim != kvc::kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "head_dim %d (need 64)", head_dim);
+  if (num_parts <= 0 || rows < 0 || num_heads <= 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad sizes");
+  if (rows == 0) return KVC_OK;
+  if (!partial_o || !partial_lse || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL pointer");
+  const hipError_t e = kvc::launch_attn_merge(dtype, num_parts, rows, num_heads, partial_o, partial_lse, o, lse,
+                                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  return KVC_OK;
+}
+
+}  // extern "C"

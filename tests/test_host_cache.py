@@ -1,0 +1,177 @@
+"""The C++ page manager behind the C ABI against the oracle, bit-exact (CPU only).
+
+Host-only handles (no device pools) run exactly the planning code that the
+device path uses, so these tests need no GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import CONTIGUOUS, FRAME_ALIGNED, OracleCache, OracleConfig, OutOfPages as OOut, NoUndo as ONo
+from oracle import is_keyframe
+from paged_sliding_window_kv_amd import KvCache, NoUndo, OutOfPages
+from paged_sliding_window_kv_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "kvc.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", hdr, re.M))
+    assert declared == set(L.EXPORTED), declared ^ set(L.EXPORTED)
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.kvc_version() >= 100
+
+
+def _pair(**kw):
+    packing = kw.pop("special_packing", FRAME_ALIGNED)
+    ocfg = OracleConfig(num_heads=1, head_dim=1, special_packing=packing, **kw)
+    oc = OracleCache(ocfg, with_pool=False)
+    hc = KvCache(num_heads=1, head_dim=1, page_size=ocfg.page_size, patch_tokens=ocfg.patch_tokens,
+                 special_tokens=ocfg.special_tokens, num_scale_units=ocfg.num_scale_units,
+                 window_units=ocfg.window_units,
+                 special_packing="contiguous" if packing == CONTIGUOUS else "frame_aligned",
+                 max_units=ocfg.max_units, num_pages=ocfg.num_pages)
+    return oc, hc
+
+
+def _same(oc, hc):
+    ids, lens = hc.visible_table()
+    oids, olens = oc.visible_table()
+    assert ids.tolist() == oids and lens.tolist() == olens
+    assert hc.state() == oc.state()
+
+
+STREAMS = [
+    dict(num_scale_units=8, window_units=64, max_units=300),                       # LingBot-Map frames
+    dict(num_scale_units=2, window_units=4, max_units=200),                        # tiny stream
+    dict(num_scale_units=2, window_units=4, max_units=200, special_packing=CONTIGUOUS),
+    dict(num_scale_units=0, window_units=4, patch_tokens=8 * 1374, special_tokens=0, max_units=40),  # chunks
+    dict(num_scale_units=0, window_units=0, patch_tokens=1374, special_tokens=0, max_units=60),      # unbounded
+    dict(num_scale_units=1, window_units=2, page_size=4, patch_tokens=6, special_tokens=3, max_units=90),
+    dict(num_scale_units=1, window_units=2, page_size=8, patch_tokens=5, special_tokens=5, max_units=90,
+         special_packing=CONTIGUOUS),
+    dict(num_scale_units=3, window_units=1, page_size=64, patch_tokens=64, special_tokens=64, max_units=50),
+]
+
+
+@pytest.mark.parametrize("kw", STREAMS)
+def test_random_ops_bit_exact(kw):
+    oc, hc = _pair(**kw)
+    rng = np.random.default_rng(11)
+    for step in range(600):
+        r = rng.random()
+        if r < 0.65:
+            try:
+                oc.append()
+                o_ok = True
+            except OOut:
+                o_ok = False
+            try:
+                hc.append()
+                h_ok = True
+            except OutOfPages:
+                h_ok = False
+            assert o_ok == h_ok
+        elif r < 0.9:
+            try:
+                oc.rollback()
+                o_ok = True
+            except ONo:
+                o_ok = False
+            try:
+                hc.rollback()
+                h_ok = True
+            except NoUndo:
+                h_ok = False
+            assert o_ok == h_ok
+        elif r < 0.93:
+            oc.reset()
+            hc.reset()
+        _same(oc, hc)
+
+
+def test_keyframe_stream_10000_bit_exact():
+    oc, hc = _pair(num_scale_units=2, window_units=4, max_units=10000)
+    for t in range(10000):
+        oc.append()
+        hc.append()
+        if not is_keyframe(t, 2, 4):
+            oc.rollback()
+            hc.rollback()
+        if t % 97 == 0 or t > 9990:
+            _same(oc, hc)
+    st = hc.state()
+    assert st["num_units"] == 2502 and len(st["special_pages"]) == 60
+    assert hc.visible_table()[1][-1] == 144
+
+
+def test_required_pages_matches_oracle():
+    from oracle import required_pages
+    for kw in STREAMS:
+        kw = dict(kw)
+        packing = kw.pop("special_packing", FRAME_ALIGNED)
+        ocfg = OracleConfig(num_heads=1, head_dim=1, special_packing=packing, **kw)
+        hc = KvCache(num_heads=1, head_dim=1, page_size=ocfg.page_size, patch_tokens=ocfg.patch_tokens,
+                     special_tokens=ocfg.special_tokens, num_scale_units=ocfg.num_scale_units,
+                     window_units=ocfg.window_units,
+                     special_packing="contiguous" if packing == CONTIGUOUS else "frame_aligned",
+                     max_units=ocfg.max_units)
+        assert hc.num_pages == required_pages(ocfg)
+
+
+def test_error_paths():
+    lib = L.lib()
+    cfg = L.KvcConfig(1, 64, 256, 0, 256, 6, 1, 2, 0, 10, 3)
+    h = C.c_void_p()
+    assert lib.kvc_create(C.byref(cfg), None, None, C.byref(h)) == 0
+    assert lib.kvc_rollback_last_frame(h) == L.KVC_ERR_NO_UNDO
+    assert lib.kvc_append_frame(h, None, None, None) == 0
+    assert lib.kvc_append_frame(h, None, None, None) == 0
+    assert lib.kvc_append_frame(h, None, None, None) == L.KVC_ERR_OUT_OF_PAGES   # 3 pages only
+    assert b"pages" in lib.kvc_last_error()
+    n = C.c_int32()
+    ids = (C.c_int32 * 1)()
+    lens = (C.c_int32 * 1)()
+    assert lib.kvc_build_visible_table(h, ids, lens, 1, C.byref(n), None) == L.KVC_ERR_BUFFER_TOO_SMALL
+    assert n.value == 3
+    # host-only handle refuses data pointers
+    assert lib.kvc_append_frame(h, C.c_void_p(16), C.c_void_p(16), None) == L.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_destroy(h) == 0
+    bad = L.KvcConfig(0, 64, 256, 0, 256, 6, 1, 2, 0, 10, 0)
+    assert lib.kvc_create(C.byref(bad), None, None, C.byref(h)) == L.KVC_ERR_INVALID_ARGUMENT
+    # device pools need head_dim 64 and page_size multiple of 64
+    odd = L.KvcConfig(1, 32, 256, 0, 256, 6, 1, 2, 0, 10, 0)
+    assert lib.kvc_create(C.byref(odd), C.c_void_p(256), C.c_void_p(256), C.byref(h)) == L.KVC_ERR_UNSUPPORTED
+    # attention argument checks run on the host
+    a = L.PagedAttnArgs()
+    a.dtype, a.num_heads, a.head_dim, a.page_size, a.sm_scale = 0, 1, 128, 256, 0.1
+    sz = C.c_size_t()
+    assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == L.KVC_ERR_UNSUPPORTED
+    a.head_dim = 64
+    a.sm_scale = float("nan")
+    assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+
+
+def test_split_choice_and_workspace():
+    lib = L.lib()
+    a = L.PagedAttnArgs()
+    a.dtype, a.num_heads, a.head_dim, a.page_size, a.sm_scale = 0, 16, 64, 256, 0.125
+    a.num_seqs, a.total_q, a.max_qo_len, a.max_kv_pages, a.num_pool_pages = 1, 262, 262, 96, 97
+    ns = C.c_int32()
+    assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0
+    assert 1 < ns.value <= 48
+    sz = C.c_size_t()
+    assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0
+    assert sz.value >= ns.value * 262 * 16 * 65 * 4
+    a.num_splits = 1
+    assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0 and sz.value == 0
+    # many query tiles: no split
+    a.num_splits, a.total_q, a.max_qo_len, a.max_kv_pages = 0, 10992, 10992, 172
+    assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 1
