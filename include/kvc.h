@@ -37,6 +37,11 @@
  *   Pool layout for a cache with H heads, head_dim d, page size P:
  *     K pool: [num_pages][H][P][d]   (slot-major rows of d elements)
  *     V pool: [num_pages][H][d][P]   (transposed: one row of P slots per dim)
+ *   Inside a V row, every group of 16 slots is stored with its middle two
+ *   4-slot groups swapped: slot s is at element
+ *     (s & ~15) | (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1)
+ *   (a self-inverse map).  This is the operand order of the attention
+ *   kernel's P*V product, so V tiles go from HBM to LDS unchanged.
  *   Element type is bf16 (2 bytes) or fp32 (4 bytes), per kvc_config.dtype.
  *   K/V/Q/O activations are [tokens][H][d], tokens in order.
  *
@@ -219,6 +224,20 @@ int paged_attn_fwd(const paged_attn_args* args, kvc_stream_t stream);
 int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
                      const float* partial_o, const float* partial_lse, void* o, float* lse,
                      kvc_stream_t stream);
+
+/* One attention step of a cache: the visible table of `cache` is built on
+ * the host and handed to the kernel inside its launch arguments (no table
+ * upload, nothing left to reuse), then q attends to every visible token
+ * ("LingBot-Map Paged KV Cache", sections 2-3: after a frame is appended its
+ * queries attend to the scale, window and special pages).  q, o: device
+ * [num_q][H][d] in the cache dtype; lse: device [num_q][H] fp32 or NULL;
+ * sm_scale <= 0 means 1/sqrt(d).  workspace: device scratch of
+ * kvc_attend_workspace_size bytes (enough for any state of this cache).
+ * KVC_ERR_UNSUPPORTED when the table has more than 640 entries: build it
+ * with kvc_build_visible_table and call paged_attn_fwd instead. */
+int kvc_attend(const kvc_t* cache, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, kvc_stream_t stream);
+int kvc_attend_workspace_size(const kvc_t* cache, int32_t num_q, size_t* bytes);
 
 const char* kvc_strerror(int status);
 const char* kvc_last_error(void);

@@ -147,17 +147,45 @@ class KvCache:
         }
 
     # -- attention ------------------------------------------------------------------
+    def workspace_bytes(self, num_q: int) -> int:
+        n = C.c_size_t()
+        L.check(L.lib().kvc_attend_workspace_size(self._h, num_q, C.byref(n)), "kvc_attend_workspace_size")
+        return n.value
+
     def attend(self, q, out=None, lse=None, sm_scale: Optional[float] = None, num_splits: int = 0,
-               stream: Optional[int] = None):
+               workspace=None, stream: Optional[int] = None):
         """Attention of q [Lq, H, d] against the visible table (one sequence).
 
-        The table is built on the host and copied to the device for the call.
-        Returns (out, lse).
+        Tables of up to 640 pages travel in the kernel arguments (kvc_attend);
+        longer ones are built on the host, copied to the device and passed to
+        paged_attn_fwd.  num_splits != 0 forces the device-table path with
+        that split count.  Returns (out, lse).
         """
-        from .attention import paged_attention
         t = _torch()
-        ids, lens = self.visible_table()
         dev = self.k_pool.device
+        if out is None:
+            out = t.empty_like(q)
+        if lse is None:
+            lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
+        n = C.c_int32()
+        L.check(L.lib().kvc_build_visible_table(self._h, None, None, 0, C.byref(n), None), "kvc_build_visible_table")
+        if num_splits == 0 and n.value <= L.MAX_INLINE_PAGES:
+            if tuple(q.shape) != (q.shape[0], self.num_heads, self.head_dim) or not q.is_contiguous():
+                raise ValueError("q must be a contiguous [Lq, H, d] tensor")
+            if q.dtype != torch_dtype(self.dtype) or q.device != dev:
+                raise ValueError(f"q must be {self.dtype} on {dev}")
+            need = self.workspace_bytes(q.shape[0])
+            if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+                workspace = t.empty(need, dtype=t.uint8, device=dev)
+            wp = workspace.data_ptr() if need else None
+            wb = workspace.numel() * workspace.element_size() if need else 0
+            s = current_stream_ptr(dev) if stream is None else stream
+            scale = 0.0 if sm_scale is None else float(sm_scale)
+            L.check(L.lib().kvc_attend(self._h, q.data_ptr(), q.shape[0], scale, out.data_ptr(), lse.data_ptr(),
+                                       wp, wb, s), "kvc_attend")
+            return out, lse
+        from .attention import paged_attention
+        ids, lens = self.visible_table()
         page_ids = t.from_numpy(ids).to(dev)
         page_lens = t.from_numpy(lens).to(dev)
         qo = t.tensor([0, q.shape[0]], dtype=t.int32, device=dev)

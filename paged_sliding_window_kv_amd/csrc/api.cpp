@@ -45,8 +45,11 @@ bool device_shapes_ok(const kvc_config& c) {
 constexpr int kXcds = 8;
 
 int choose_waves(const paged_attn_args& a) {
-  // 8 waves (256 query rows) once there are enough rows to fill them.
-  return a.max_qo_len >= 1024 ? 8 : 4;
+  // Up to 256 query rows: one wave per 32 rows, all in one workgroup, so each
+  // key tile is read once per split.  Beyond that: 288-row workgroups (eight
+  // waves plus the block their first four share), returned as 9.
+  if (a.max_qo_len <= 256) return std::max(1, (a.max_qo_len + 31) / 32);
+  return 9;
 }
 
 int rows_per_tile(const paged_attn_args& a) {
@@ -58,9 +61,11 @@ int choose_splits(const paged_attn_args& a) {
   if (a.max_kv_pages <= 1) return 1;
   const int rows = rows_per_tile(a);
   const long tiles = static_cast<long>((a.max_qo_len + rows - 1) / rows) * a.num_seqs * a.num_heads;
-  // Aim for about two workgroups per compute unit (256 CUs), keeping at least
-  // two pages per split so the merge traffic stays small against K/V reads.
-  const long target = 512;
+  // Aim for about one round of workgroups over the 256 compute units (two per
+  // unit for narrow workgroups), keeping at least two pages per split so the
+  // merge traffic stays small against the K/V reads.
+  const int waves = a.dtype == KVC_DTYPE_BF16 ? choose_waves(a) : 1;
+  const long target = waves <= 4 ? 512 : 256;
   if (tiles >= target) return 1;
   long s = (target + tiles - 1) / tiles;
   s = std::min<long>(s, std::max(1, a.max_kv_pages / 2));
@@ -243,6 +248,90 @@ int paged_attn_num_splits(const paged_attn_args* a, int32_t* num_splits) {
   return KVC_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fills the kernel parameters shared by both table sources; returns the
+// split count through *splits_out.
+int setup_attn(const paged_attn_args& a, kvc::AttnParams& p, int* splits_out) {
+  const int splits = choose_splits(a);
+  const size_t need = workspace_for(a, splits);
+  if (need > 0 && (!a.workspace || a.workspace_bytes < need))
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes", need);
+  const int rows = rows_per_tile(a);
+  const long q_tiles = (a.max_qo_len + rows - 1) / rows;
+  const long groups = static_cast<long>(a.num_seqs) * a.num_heads * splits;
+  const long groups_padded = (groups + kXcds - 1) / kXcds * kXcds;
+  if (q_tiles * groups_padded > 0x7fffffffL) return fail(KVC_ERR_UNSUPPORTED, "grid too large");
+  p = kvc::AttnParams{};
+  p.q = a.q;
+  p.k_pool = a.k_pool;
+  p.v_pool = a.v_pool;
+  p.o = a.o;
+  p.lse = a.lse;
+  if (splits > 1) {
+    const size_t rh = static_cast<size_t>(a.total_q) * a.num_heads;
+    p.part_o = static_cast<float*>(a.workspace);
+    const size_t obytes = (static_cast<size_t>(splits) * rh * kvc::kHeadDim * sizeof(float) + 255) & ~size_t(255);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + obytes);
+  }
+  p.qo_indptr = a.qo_indptr;
+  p.kv_indptr = a.kv_indptr;
+  p.page_ids = a.page_ids;
+  p.page_lens = a.page_lens;
+  p.num_heads = a.num_heads;
+  p.page_size = a.page_size;
+  p.num_pool_pages = a.num_pool_pages;
+  p.num_seqs = a.num_seqs;
+  p.total_q = a.total_q;
+  p.q_tiles = static_cast<int32_t>(q_tiles);
+  p.num_splits = splits;
+  p.groups = static_cast<int32_t>(groups);
+  p.groups_padded = static_cast<int32_t>(groups_padded);
+  p.sm_scale = a.sm_scale;
+  p.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  *splits_out = splits;
+  return KVC_OK;
+}
+
+template <class Src>
+int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_t st) {
+  const kvc::AttnParams& p = kvc::attn_base(src);
+  hipError_t e = a.dtype == KVC_DTYPE_BF16 ? kvc::launch_attn_bf16(src, choose_waves(a), st)
+                                           : kvc::launch_attn_f32(src, st);
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
+  if (splits > 1) {
+    e = kvc::launch_attn_merge(a.dtype, splits, a.total_q, a.num_heads, p.part_o, p.part_lse, a.o, a.lse, st);
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  }
+  return KVC_OK;
+}
+
+// Attention arguments of one cache-level step (single sequence, table inline).
+paged_attn_args cache_attn_args(const kvc_t* c, int32_t num_q, int32_t num_entries, float sm_scale) {
+  const kvc_config& cfg = c->pc.config();
+  paged_attn_args a{};
+  a.dtype = cfg.dtype;
+  a.num_heads = cfg.num_heads;
+  a.head_dim = cfg.head_dim;
+  a.page_size = cfg.page_size;
+  a.sm_scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt(static_cast<float>(cfg.head_dim));
+  a.num_seqs = 1;
+  a.total_q = num_q;
+  a.max_qo_len = num_q;
+  a.max_kv_pages = num_entries;
+  a.num_pool_pages = c->pc.num_pages();
+  a.num_splits = 0;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
 int paged_attn_fwd(const paged_attn_args* a, kvc_stream_t stream) {
   if (int s = check_attn_args(a)) return s;
   if (a->num_seqs == 0 || a->total_q == 0 || a->max_qo_len == 0) return KVC_OK;
@@ -250,52 +339,51 @@ int paged_attn_fwd(const paged_attn_args* a, kvc_stream_t stream) {
     return fail(KVC_ERR_INVALID_ARGUMENT, "NULL device pointer");
   if (a->max_kv_pages > 0 && (!a->page_ids || !a->page_lens || !a->k_pool || !a->v_pool))
     return fail(KVC_ERR_INVALID_ARGUMENT, "NULL table or pool pointer");
-  const int splits = choose_splits(*a);
-  const size_t need = workspace_for(*a, splits);
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
-    return fail(KVC_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes", need);
-  const int rows = rows_per_tile(*a);
-  const long q_tiles = (a->max_qo_len + rows - 1) / rows;
-  const long groups = static_cast<long>(a->num_seqs) * a->num_heads * splits;
-  const long groups_padded = (groups + kXcds - 1) / kXcds * kXcds;
-  if (q_tiles * groups_padded > 0x7fffffffL) return fail(KVC_ERR_UNSUPPORTED, "grid too large");
+  kvc::AttnParams p;
+  int splits = 1;
+  if (int s = setup_attn(*a, p, &splits)) return s;
+  return launch_attn(*a, p, splits, reinterpret_cast<hipStream_t>(stream));
+}
 
-  kvc::AttnParams p{};
-  p.q = a->q;
-  p.k_pool = a->k_pool;
-  p.v_pool = a->v_pool;
-  p.o = a->o;
-  p.lse = a->lse;
-  if (splits > 1) {
-    const size_t rh = static_cast<size_t>(a->total_q) * a->num_heads;
-    p.part_o = static_cast<float*>(a->workspace);
-    const size_t obytes = (static_cast<size_t>(splits) * rh * kvc::kHeadDim * sizeof(float) + 255) & ~size_t(255);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + obytes);
-  }
-  p.qo_indptr = a->qo_indptr;
-  p.kv_indptr = a->kv_indptr;
-  p.page_ids = a->page_ids;
-  p.page_lens = a->page_lens;
-  p.num_heads = a->num_heads;
-  p.page_size = a->page_size;
-  p.num_pool_pages = a->num_pool_pages;
-  p.num_seqs = a->num_seqs;
-  p.total_q = a->total_q;
-  p.q_tiles = static_cast<int32_t>(q_tiles);
-  p.num_splits = splits;
-  p.groups = static_cast<int32_t>(groups);
-  p.groups_padded = static_cast<int32_t>(groups_padded);
-  p.sm_scale = a->sm_scale;
-  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = a->dtype == KVC_DTYPE_BF16 ? kvc::launch_attn_bf16(p, choose_waves(*a), st)
-                                            : kvc::launch_attn_f32(p, st);
-  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
-  if (splits > 1) {
-    e = kvc::launch_attn_merge(a->dtype, splits, a->total_q, a->num_heads, p.part_o, p.part_lse, a->o, a->lse, st);
-    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
-  }
+int kvc_attend_workspace_size(const kvc_t* c, int32_t num_q, size_t* bytes) {
+  if (!c || !bytes || num_q < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad argument");
+  const int32_t max_entries = std::min<int32_t>(c->pc.num_pages(), kvc::kMaxInlinePages);
+  const paged_attn_args a = cache_attn_args(c, num_q, max_entries, 0.f);
+  if (int s = check_attn_args(&a)) return s;
+  *bytes = workspace_for(a, choose_splits(a));
   return KVC_OK;
+}
+
+int kvc_attend(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache has no device pools");
+  if (num_q < 0 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "bad num_q or sm_scale");
+  if (num_q == 0) return KVC_OK;
+  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
+  const int32_t n = c->pc.visible_count();
+  if (n > kvc::kMaxInlinePages)
+    return fail(KVC_ERR_UNSUPPORTED, "visible table has %d pages; kvc_attend passes at most %d (use paged_attn_fwd)",
+                n, kvc::kMaxInlinePages);
+  if (c->pc.num_pages() > kvc::kInlineMaxPid + 1 || c->pc.config().page_size > 4095)
+    return fail(KVC_ERR_UNSUPPORTED, "pool too large for inline tables");
+  paged_attn_args a = cache_attn_args(c, num_q, n, sm_scale);
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (int s = check_attn_args(&a)) return s;
+  static thread_local kvc::AttnParamsInline pi;
+  int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
+  c->pc.visible_table(ids, lens);
+  int splits = 1;
+  if (int s = setup_attn(a, pi.base, &splits)) return s;
+  pi.num_entries = n;
+  for (int32_t i = 0; i < n; ++i)
+    pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
+  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
 }
 
 int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,

@@ -24,7 +24,9 @@ constexpr int KT = kKeyTile;
 constexpr int ROWS = 64;
 constexpr int KB = 16;
 
-__global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
+template <class Src>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const Src src) {
+  const AttnParams& p = attn_base(src);
   __shared__ __attribute__((aligned(16))) float lk[KT * D];
   __shared__ __attribute__((aligned(16))) float lv[D * KT];
 
@@ -36,12 +38,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   const int sh = g / p.num_splits;
   const int h = sh % p.num_heads;
   const int seq = sh / p.num_heads;
-  const int q0 = p.qo_indptr[seq];
-  const int qn = p.qo_indptr[seq + 1] - q0;
+  int q0, qn, ebase, ecount;
+  attn_seq(src, seq, q0, qn, ebase, ecount);
   const int row0 = qt * ROWS;
   if (row0 >= qn) return;
-  const int ebase = p.kv_indptr[seq];
-  const int ecount = p.kv_indptr[seq + 1] - ebase;
   const int per = (ecount + p.num_splits - 1) / p.num_splits;
   const int eb = ebase + min(ecount, split * per);
   const int ee = ebase + min(ecount, (split + 1) * per);
@@ -72,10 +72,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   for (int e = eb; e < ee; ++e) {
-    const int pid = p.page_ids[e];
-    int len = p.page_lens[e];
-    len = len < 0 ? 0 : (len > P ? P : len);
-    if (pid < 0 || pid >= p.num_pool_pages) len = 0;
+    int pid, len;
+    attn_entry(src, e, pid, len);
     for (int kt = 0; kt * KT < len; ++kt) {
       const int nk = min(KT, len - kt * KT);
       __syncthreads();
@@ -83,13 +81,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
       const float* vb = vg + (static_cast<size_t>(pid) * H + h) * D * P + kt * KT;
       for (int c = lane; c < KT * D / 4; c += 64) {
         reinterpret_cast<float4*>(lk)[c] = reinterpret_cast<const float4*>(kb)[c];
-        const int dd = c / (KT / 4), k4 = (c % (KT / 4)) * 4;
-        float4 v = *reinterpret_cast<const float4*>(vb + static_cast<size_t>(dd) * P + k4);
+        // pool elements 4c'..4c'+3 of a V^T row hold slots v_slot_pos(4c')..+3
+        const int dd = c / (KT / 4), p4 = (c % (KT / 4)) * 4;
+        const int k4 = v_slot_pos(p4);
+        float4 v = *reinterpret_cast<const float4*>(vb + static_cast<size_t>(dd) * P + p4);
         if (k4 + 0 >= nk) v.x = 0.f;
         if (k4 + 1 >= nk) v.y = 0.f;
         if (k4 + 2 >= nk) v.z = 0.f;
         if (k4 + 3 >= nk) v.w = 0.f;
-        reinterpret_cast<float4*>(lv)[c] = v;
+        *reinterpret_cast<float4*>(lv + dd * KT + k4) = v;
       }
       __syncthreads();
       for (int j0 = 0; j0 < nk; j0 += KB) {
@@ -159,10 +159,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 
 int attn_f32_rows_per_tile() { return ROWS; }
 
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
+template <class Src>
+static hipError_t launch_impl(const Src& src, hipStream_t stream) {
+  const AttnParams& p = attn_base(src);
   const dim3 grid(static_cast<unsigned>(p.q_tiles) * p.groups_padded);
-  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((attn_f32_kernel<Src>), grid, dim3(64), 0, stream, src);
   return hipGetLastError();
 }
+
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) { return launch_impl(p, stream); }
+hipError_t launch_attn_f32(const AttnParamsInline& p, hipStream_t stream) { return launch_impl(p, stream); }
 
 }  // namespace kvc

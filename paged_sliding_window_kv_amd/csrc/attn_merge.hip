@@ -8,7 +8,8 @@
 // the output is 0 and lse is -inf.
 //
 // One thread per (row, head, dim); 64 consecutive threads read one part's
-// 256-byte row, so every access is coalesced.
+// 256-byte row, so every access is coalesced, and each thread keeps eight
+// parts' loads in flight at once.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,15 +40,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int parts, int rows_hea
   const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int d = threadIdx.x & 63;
   if (rh >= rows_heads) return;
-  float m = -INFINITY;
-  for (int i = 0; i < parts; ++i) m = fmaxf(m, plse[static_cast<size_t>(i) * rows_heads + rh]);
-  float z = 0.f, acc = 0.f;
-  if (m != -INFINITY) {
-    for (int i = 0; i < parts; ++i) {
-      const float li = plse[static_cast<size_t>(i) * rows_heads + rh];
-      const float w = li == -INFINITY ? 0.f : __expf(li - m);
+  // Parts are consumed in batches of 8 whose loads are all issued together;
+  // the running maximum m keeps the weights finite across batches.
+  constexpr int B = 8;
+  float m = -INFINITY, z = 0.f, acc = 0.f;
+  for (int i0 = 0; i0 < parts; i0 += B) {
+    float li[B], oi[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = i0 + j;
+      const bool ok = i < parts;
+      li[j] = ok ? plse[static_cast<size_t>(i) * rows_heads + rh] : -INFINITY;
+      oi[j] = ok ? po[(static_cast<size_t>(i) * rows_heads + rh) * D + d] : 0.f;
+    }
+    float mb = li[0];
+#pragma unroll
+    for (int j = 1; j < B; ++j) mb = fmaxf(mb, li[j]);
+    if (mb == -INFINITY) continue;
+    if (mb > m) {
+      const float c = m == -INFINITY ? 0.f : __expf(m - mb);
+      z *= c;
+      acc *= c;
+      m = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const float w = li[j] == -INFINITY ? 0.f : __expf(li[j] - m);
       z += w;
-      acc = __builtin_fmaf(w, po[(static_cast<size_t>(i) * rows_heads + rh) * D + d], acc);
+      acc = __builtin_fmaf(w, oi[j], acc);
     }
   }
   const float out = z > 0.f ? acc / z : 0.f;

@@ -8,6 +8,12 @@
 
 namespace kvc {
 
+// V pools store each [dim][slot] row with the middle two 4-slot groups of
+// every 16-slot group swapped: slot s lives at element v_slot_pos(s).  The
+// map is its own inverse.  (It makes a 16-byte chunk of a row one operand
+// fragment of the bf16 kernel's P*V product.)
+__host__ __device__ constexpr int v_slot_pos(int s) { return (s & ~15) | (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
 // Most pages one unit may span (one chunk of 8 VGGT frames is 43 pages).
 constexpr int kMaxUnitPages = 256;
 // Head dim and key tile of the device kernels.
@@ -61,11 +67,68 @@ struct AttnParams {
   float scale_log2;       // sm_scale * log2(e)
 };
 
+// Most table entries passed by value in the kernel arguments (single
+// sequence).  Each entry packs page id (low 20 bits) and valid length (high
+// 12 bits); with the parameters above the argument block stays under 3 KiB.
+constexpr int kMaxInlinePages = 640;
+constexpr int kInlinePidBits = 20;
+constexpr int kInlineMaxPid = (1 << kInlinePidBits) - 1;
+
+// Paged attention of one sequence whose table travels in the kernel
+// arguments: queries [0, total_q), entries [0, num_entries).
+struct AttnParamsInline {
+  AttnParams base;
+  int32_t num_entries;
+  uint32_t entries[kMaxInlinePages];
+};
+
+// Table access shared by the attention kernels, for both table sources.
+__host__ __device__ __forceinline__ const AttnParams& attn_base(const AttnParams& p) { return p; }
+__host__ __device__ __forceinline__ const AttnParams& attn_base(const AttnParamsInline& p) { return p.base; }
+
+// Device tables are read through the constant address space: the reads are
+// wave-uniform, so they become scalar loads, which leave the vector-memory
+// wait counts of the attention kernels to the K/V tile loads alone.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, int i) {
+  return reinterpret_cast<const_i32*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
+__device__ __forceinline__ void attn_seq(const AttnParams& p, int seq, int& q0, int& qn, int& e0, int& en) {
+  q0 = ld_const(p.qo_indptr, seq);
+  qn = ld_const(p.qo_indptr, seq + 1) - q0;
+  e0 = ld_const(p.kv_indptr, seq);
+  en = ld_const(p.kv_indptr, seq + 1) - e0;
+}
+__device__ __forceinline__ void attn_seq(const AttnParamsInline& p, int, int& q0, int& qn, int& e0, int& en) {
+  q0 = 0;
+  qn = p.base.total_q;
+  e0 = 0;
+  en = p.num_entries;
+}
+
+// Page id and valid length of table entry e; invalid ids and lengths give 0.
+__device__ __forceinline__ void attn_entry(const AttnParams& p, int e, int& pid, int& len) {
+  pid = ld_const(p.page_ids, e);
+  len = ld_const(p.page_lens, e);
+  len = len < 0 ? 0 : (len > p.page_size ? p.page_size : len);
+  if (pid < 0 || pid >= p.num_pool_pages) len = 0;
+}
+__device__ __forceinline__ void attn_entry(const AttnParamsInline& p, int e, int& pid, int& len) {
+  const uint32_t w = p.entries[e];
+  pid = static_cast<int>(w & kInlineMaxPid);
+  len = static_cast<int>(w >> kInlinePidBits);
+  len = len > p.base.page_size ? p.base.page_size : len;
+  if (pid >= p.base.num_pool_pages) len = 0;
+}
+
 // Rows of queries one workgroup of the bf16 kernel covers.
 int attn_bf16_rows_per_tile(int waves);
 hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParamsInline& p, int waves, hipStream_t stream);
 int attn_f32_rows_per_tile();
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParamsInline& p, hipStream_t stream);
 
 hipError_t launch_attn_merge(int dtype, int num_parts, int rows, int num_heads, const float* part_o,
                              const float* part_lse, void* o, float* lse, hipStream_t stream);

@@ -1,4 +1,5 @@
 // KV-append scatter: one unit's K/V rows into its pages.
+// V rows are written in the pool's slot order (v_slot_pos).
 //
 // "LingBot-Map Paged KV Cache", section 2: a frame's 256 patch tokens fill one
 // page of the patch stream and its 6 special tokens are packed into the
@@ -83,16 +84,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const AppendParams 
   // Fast path: the whole tile lands on consecutive slots of one page.
   const Dest first = dest_of(p, tok0);
   const Dest last = dest_of(p, tok0 + ntok - 1);
-  const bool run = first.page == last.page && last.slot - first.slot == ntok - 1 && (first.slot % VEC) == 0 &&
-                   (ntok % VEC) == 0;
+  const bool run = first.page == last.page && last.slot - first.slot == ntok - 1 && (first.slot % 16) == 0 &&
+                   (ntok % 16) == 0;
   if (run) {
     const int groups = ntok / VEC;  // 16-byte runs per dim row
     for (int c = threadIdx.x; c < D * groups; c += kThreads) {
       const int d = c / groups, g = c % groups;
       V16 out;
       T* oe = reinterpret_cast<T*>(&out);
+      // element g*VEC + e of the run holds slot v_slot_pos(g*VEC + e) (runs start 16-aligned)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) oe[e] = vt[g * VEC + e][d];
+      for (int e = 0; e < VEC; ++e) oe[e] = vt[v_slot_pos(g * VEC + e)][d];
       const size_t dst = ((static_cast<size_t>(first.page) * H + h) * D + d) * P + first.slot + g * VEC;
       *reinterpret_cast<V16*>(vpool + dst) = out;
     }
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const AppendParams 
     for (int c = threadIdx.x; c < D * ntok; c += kThreads) {
       const int d = c / ntok, t = c % ntok;
       const Dest dd = dest_of(p, tok0 + t);
-      const size_t dst = ((static_cast<size_t>(dd.page) * H + h) * D + d) * P + dd.slot;
+      const size_t dst = ((static_cast<size_t>(dd.page) * H + h) * D + d) * P + v_slot_pos(dd.slot);
       vpool[dst] = vt[t][d];
     }
   }

@@ -67,5 +67,25 @@ def check_attention(o_dev, lse_dev, o_ref, lse_ref, dtype: str, what: str = ""):
             assert le <= lse_tol, f"{what}: lse error {le}"
 
 
+def v_slot_pos(s: int) -> int:
+    """Element of a V pool row that holds slot s (the layout include/kvc.h documents)."""
+    return (s & ~15) | (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1)
+
+
+def v_positions(page_size: int) -> np.ndarray:
+    return np.array([v_slot_pos(s) for s in range(page_size)], np.int64)
+
+
+def v_pool_device_layout(v_nat: np.ndarray) -> np.ndarray:
+    """[N, H, P, d] natural V pages -> [N, H, d, P] device layout (rows in pool slot order)."""
+    vt = np.ascontiguousarray(v_nat.transpose(0, 1, 3, 2))
+    return np.ascontiguousarray(vt[..., v_positions(vt.shape[-1])])  # map is its own inverse
+
+
+def v_pool_natural(v_dev: np.ndarray) -> np.ndarray:
+    """[N, H, d, P] device layout -> [N, H, P, d] natural V pages."""
+    return np.ascontiguousarray(v_dev[..., v_positions(v_dev.shape[-1])].transpose(0, 1, 3, 2))
+
+
 def unit_qkv(seed, layer, t, tokens, heads, head_dim, dtype, q_scale=1.0):
     return synth.frame_qkv(seed, layer, t, tokens, heads, head_dim, dtype, q_scale)

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import log, to_dev, to_host_bits
+from gpu_helpers import log, to_dev, to_host_bits, v_pool_natural
 from oracle import CONTIGUOUS, FRAME_ALIGNED, OracleCache, OracleConfig, is_keyframe
 
 pytestmark = pytest.mark.gpu
@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 def _compare_pools(dc, oc, dtype):
     kd = to_host_bits(dc.k_pool, dtype)                       # [N, H, P, d]
-    vd = to_host_bits(dc.v_pool, dtype).transpose(0, 1, 3, 2)  # [N, H, d, P] -> [N, H, P, d]
+    vd = v_pool_natural(to_host_bits(dc.v_pool, dtype))      # [N, H, d, P] -> [N, H, P, d]
     ids, lens = oc.visible_table()
     assert dc.visible_table()[0].tolist() == ids
     for p, n in zip(ids, lens):

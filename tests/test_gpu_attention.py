@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import check_attention, log, to_dev, to_f64
+from gpu_helpers import check_attention, log, to_dev, to_f64, v_pool_device_layout, v_positions
 from oracle import OracleCache, OracleConfig, attention_f64, is_keyframe, merge_partials
 from oracle import to_f64 as bits_f64
 
@@ -112,11 +112,12 @@ def test_multi_sequence_ragged(dtype):
     vpool = synth.normal_tokens(3, 0, 0, 2, N * H * P, 1, 64, dtype).reshape(N, H, P, 64)
     q = synth.normal_tokens(3, 0, 0, 0, int(qo[-1]), H, 64, dtype)
     kd = to_dev(kpool, dtype)
-    vd = to_dev(np.ascontiguousarray(vpool.transpose(0, 1, 3, 2)), dtype)
+    vd = to_dev(v_pool_device_layout(vpool), dtype)
     # stale slots past each page's length become NaN on the device
+    pos = torch.from_numpy(v_positions(P)).cuda()
     for p, n in zip(ids, lens):
         kd[p, :, n:] = float("nan")
-        vd[p, :, :, n:] = float("nan")
+        vd[p][:, :, pos[n:]] = float("nan")
     dev = lambda a: torch.from_numpy(a).cuda()
     for splits in (0, 1, 4):
         o, lse = paged_attention(to_dev(q, dtype), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
@@ -160,8 +161,7 @@ def test_page_order_and_placement_invariance():
     gv = np.concatenate([vpool[p, :, :n] for p, n in zip(ids, lens)], axis=1)
     ro, rl = attention_f64(bits_f64(q), bits_f64(gk), bits_f64(gv))
     for kp, vp, ii, ll in ((kpool, vpool, ids, lens), (kpool2, vpool2, new_ids, lens[perm])):
-        o, lse = paged_attention(to_dev(q, "bf16"), to_dev(kp, "bf16"),
-                                 to_dev(np.ascontiguousarray(vp.transpose(0, 1, 3, 2)), "bf16"),
+        o, lse = paged_attention(to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(v_pool_device_layout(vp), "bf16"),
                                  dev(ii), dev(ll), dev(qo), dev(kv), max_qo_len=200, max_kv_pages=npg)
         check_attention(o, lse, ro, rl, "bf16", "placement")
 
