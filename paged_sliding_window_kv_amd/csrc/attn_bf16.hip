@@ -10,8 +10,8 @@
 //
 // Mapping to the hardware
 //  * One workgroup = NB waves covering NB*32 query rows of one (sequence,
-//    head, key split), each wave owning 32 rows whose Q fragment stays in
-//    registers for the whole key loop.  Variant NB = 8 + extra block covers
+//    head, key split), each wave owning 32 rows.  The tile's queries sit in
+//    LDS; Q fragments are re-read there every 128-key step.  Variant NB = 8 + extra block covers
 //    288 rows (the 262 queries of a frame fit one workgroup): the ninth
 //    32-row block is shared by waves 0..3, each taking one 32-key quarter of
 //    every 128-key step, so each SIMD carries the same load (2.25 blocks);
@@ -73,6 +73,9 @@ constexpr int DMA_PER_TILE = 16;    // 1 KiB global->LDS loads per tile (8 for K
 // open, and lgkmcnt(0) with the others left open.
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkmcnt0 = 0xC07F;
+// Headroom (log2 units) the running maximum may lag the true one before the
+// output accumulator is rescaled.
+constexpr float kRescaleSlack = 8.f;
 
 // 16-byte chunk c of LDS row r is stored at physical chunk c ^ swz(r).  Rows
 // are 128 bytes, so 16 consecutive rows read at the same logical chunk cover
@@ -183,6 +186,7 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   constexpr int ROWS = (NB + (XB ? 1 : 0)) * 32;
   constexpr int LPT = (DMA_PER_TILE + NB - 1) / NB;  // direct loads per wave per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[STAGES][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[ROWS * D];  // this tile's queries, swizzled rows
 
   // ---- which (sequence, head, split, query tile) ----------------------------
   const int L = blockIdx.x;
@@ -227,20 +231,18 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   const size_t page_stride = static_cast<size_t>(H) * P * D;  // elements per page (K or V)
   const size_t head_off = static_cast<size_t>(h) * P * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16*st + 8*lh .. +7] ----
-  auto load_q = [&](int row, bool ok, bf16x8* f) {
-    const uint16_t* qp = qg + (static_cast<size_t>(q0 + (ok ? row : 0)) * H + h) * D + 8 * lh;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qp + 16 * st) : i32x4{0, 0, 0, 0};
-      f[st] = __builtin_bit_cast(bf16x8, v);
-    }
-  };
-  bf16x8 qf[4], qx[4];
-  load_q(qrow, qvalid, qf);
-  if (XB) load_q(xrow, xvalid && xactive, qx);
+  // ---- queries of the tile -> LDS (rows past the sequence are zero) ----------
+  // Q fragments (B operand of S^T = K Q^T: Q[row][16*st + 8*lh .. +7]) are read
+  // from here at every 128-key step rather than held in registers.
+  for (int c = tid; c < ROWS * 8; c += NB * 64) {
+    const int r = c >> 3, ch = c & 7;
+    const int row = row0 + r;
+    i32x4 v = {0, 0, 0, 0};
+    if (row < qn) v = *reinterpret_cast<const i32x4*>(qg + (static_cast<size_t>(q0 + row) * H + h) * D + ch * 8);
+    *reinterpret_cast<i32x4*>(lds_q + r * D + ((ch ^ swz(r)) << 3)) = v;
+  }
   // Settle the Q loads before the ring starts, so that the wait counts below
-  // cover tile loads only.
+  // cover tile loads only (the first ring barrier publishes lds_q).
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
   // ---- this wave's share of each tile's 16 direct loads -----------------------
@@ -342,17 +344,43 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
     }
 
     if (active) {
-      // One 64-key tile: S^T blocks s0 (keys 0..31) and s1 (keys 32..63).
-      auto own_tile = [&](const uint16_t* lk, const uint16_t* lv, int nk) {
-        floatx16 s0 = {}, s1 = {};
-        __builtin_amdgcn_s_setprio(1);
+      bf16x8 qf[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) qf[st] = lds_frag(lds_q, wave * 32 + lr, 2 * st + lh);
+      // Operand fragments of a product group are all read from LDS before its
+      // first MFMA, so the matrix pipe is not left waiting on each read.
+      auto qk = [&](const uint16_t* lk, floatx16& s0, floatx16& s1) {
+        bf16x8 ka[4], kb[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lk, lr, 2 * st + lh), qf[st], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lk, 32 + lr, 2 * st + lh), qf[st], s1, 0, 0, 0);
+          ka[st] = lds_frag(lk, lr, 2 * st + lh);
+          kb[st] = lds_frag(lk, 32 + lr, 2 * st + lh);
         }
-        __builtin_amdgcn_s_setprio(0);
-        if (nk < KT) {
+        s0 = floatx16{};
+        s1 = floatx16{};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st], qf[st], s1, 0, 0, 0);
+        }
+      };
+      auto pv = [&](const floatx16& s0, const floatx16& s1, const uint16_t* lv) {
+        bf16x8 va[4], vb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          va[t] = lds_frag(lv, lr, 2 * t + lh);
+          vb[t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 pb = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
+          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb, o0, 0, 0, 0);
+          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[t], pb, o1, 0, 0, 0);
+        }
+      };
+      // Softmax update of one tile's scores, in place (scores -> probabilities).
+      auto soft = [&](floatx16& s0, floatx16& s1, int nk, bool full) {
+        if (!full && nk < KT) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
@@ -361,8 +389,11 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
           }
         }
         const float mx = pair_max(tile_max(s0, s1)) * sl2;
-        // Rescale only when some row's maximum grew; otherwise every factor is 1.
-        if (__any(mx > m_run)) {
+        // The reference maximum only moves when a row's maximum exceeds it by
+        // more than kRescaleSlack (log2 units): probabilities stay <= 2^slack,
+        // far from fp32 or bf16 overflow, and the final division by the row
+        // sum is exact whichever reference was used.
+        if (__any(mx > m_run + kRescaleSlack)) {
           const float m_new = fmaxf(m_run, mx);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
@@ -380,17 +411,35 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
           s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, nm));
         }
         l_run += tile_sum(s0, s1);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 pb = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lv, lr, 2 * t + lh), pb, o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lv, 32 + lr, 2 * t + lh), pb, o1, 0, 0, 0);
-        }
-        __builtin_amdgcn_s_setprio(0);
       };
-      own_tile(lka, lva, nka);
-      if (two) own_tile(lkb, lvb, nkb);
+      floatx16 a0, a1, b0, b1;
+      if (two && nka == KT && nkb == KT) {
+        // Full pair: one straight-line block.  Waves w and w+4 share a SIMD;
+        // the upper half takes the pair in the opposite order so that one
+        // wave's softmax arithmetic tends to run under the other's products.
+        const bool rev = (wave & 4) != 0;
+        const uint16_t* k1 = rev ? lkb : lka;
+        const uint16_t* k2 = rev ? lka : lkb;
+        const uint16_t* v1 = rev ? lvb : lva;
+        const uint16_t* v2 = rev ? lva : lvb;
+        __builtin_amdgcn_s_setprio(1);
+        qk(k1, a0, a1);
+        qk(k2, b0, b1);
+        __builtin_amdgcn_s_setprio(0);
+        soft(a0, a1, KT, true);
+        pv(a0, a1, v1);
+        soft(b0, b1, KT, true);
+        pv(b0, b1, v2);
+      } else {
+        qk(lka, a0, a1);
+        soft(a0, a1, nka, false);
+        pv(a0, a1, lva);
+        if (two) {
+          qk(lkb, b0, b1);
+          soft(b0, b1, nkb, false);
+          pv(b0, b1, lvb);
+        }
+      }
     }
 
     if (XB && xactive) {
@@ -404,7 +453,8 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lk, 32 * kb + lr, 2 * st + lh), qx[st], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lk, 32 * kb + lr, 2 * st + lh),
+                                                      lds_frag(lds_q, NB * 32 + lr, 2 * st + lh), s, 0, 0, 0);
         __builtin_amdgcn_s_setprio(0);
         if (nkt < 32 * kb + 32) {
 #pragma unroll
@@ -414,7 +464,7 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
           }
         }
         const float mx = pair_max(half_max(s)) * sl2;
-        if (__any(mx > xm)) {
+        if (__any(mx > xm + kRescaleSlack)) {
           const float m_new = fmaxf(xm, mx);
           const float alpha = __builtin_amdgcn_exp2f(xm - m_new);
           xm = m_new;
