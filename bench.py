@@ -274,14 +274,218 @@ def run_stream(args) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# VGGT-style chunked global attention and full global + frame attention
+# ----------------------------------------------------------------------------
+VGGT_TOKENS = 1374
+CHUNK = dict(layers=24, heads=16, d=64, page=256, frames_per_chunk=8, window_chunks=4)
+
+
+def run_chunked(args) -> dict:
+    """Chunks of 8 frames (10,992 tokens, 43 pages) attend to the last 4 chunks (43,968 keys)."""
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, lib
+    c = CHUNK
+    L = c["layers"]
+    tokens = c["frames_per_chunk"] * VGGT_TOKENS
+    W = c["window_chunks"]
+    steps, warm = args.steps, max(args.warmup, W)
+    log(f"[bench] chunked: {L} layers, chunk {tokens} tokens, window {W} chunks, warmup {warm}, timed {steps}")
+    dev = torch.device("cuda:0")
+    lb = lib()
+    caches = [KvCache(num_heads=c["heads"], dtype="bf16", patch_tokens=tokens, special_tokens=0, num_scale_units=0,
+                      window_units=W, max_units=warm + steps, device=dev) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    bank = 2
+    shp = (bank, tokens, c["heads"], c["d"])
+    qs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    ks = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    vs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    out = torch.empty((tokens, c["heads"], c["d"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((tokens, c["heads"]), dtype=torch.float32, device=dev)
+    wsb = max(cc.workspace_bytes(tokens) for cc in caches)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i, events=None):
+        b = i % bank
+        for l in range(L):
+            _ok(lb.kvc_append_frame(caches[l].handle, ks[l][b].data_ptr(), vs[l][b].data_ptr(), sp), "append")
+            if events is not None:
+                events[2 * l].record()
+            _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), tokens, 0.0, out.data_ptr(), lse.data_ptr(),
+                              ws.data_ptr(), wsb, sp), "attend")
+            if events is not None:
+                events[2 * l + 1].record()
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    lk = W * tokens
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warm + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    flops = steps * L * attn_flops(tokens, lk, c["heads"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+    att = 0.0
+    for i in range(steps):
+        step(warm + steps + i, ev)
+        ev[-1].synchronize()
+        att += sum(ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L)) * 1e-3
+    n = steps * L
+    ach = flops / att / 1e12
+    tf = flops / el / 1e12
+    log(f"[bench] chunked: {el / steps * 1e3:.2f} ms/step, {tf:.1f} TFLOP/s, attention calls {att / n * 1e6:.1f} us avg, "
+        f"{ach:.1f} TFLOP/s ({ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
+    return {
+        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3,
+        "frames_per_s": steps * c["frames_per_chunk"] / el,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+        "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, bf16, chunks of 8 x 1374 = {tokens} "
+                               f"tokens, window 4 chunks ({lk} visible keys), {steps} timed chunk steps",
+                   "layers": L, "heads": 16, "head_dim": 64, "chunk_tokens": tokens, "visible_tokens": lk},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "paged attention call (attn_bf16_kernel)", "avg_call_us": att / n * 1e6,
+                     "calls": n},
+    }
+
+
+def run_global(args) -> dict:
+    """100 frames x 1374 tokens: global attention over all 137,400 tokens, then per-frame attention."""
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, lib, paged_attention
+    frames, L, H = 100, 24, 16
+    T = frames * VGGT_TOKENS
+    steps = max(1, args.steps)
+    log(f"[bench] global: {L} layers, {frames} frames x {VGGT_TOKENS} tokens = {T}, timed {steps} pass(es)")
+    dev = torch.device("cuda:0")
+    lb = lib()
+    caches = [KvCache(num_heads=H, dtype="bf16", patch_tokens=VGGT_TOKENS, special_tokens=0, num_scale_units=0,
+                      window_units=0, max_units=frames, device=dev) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    q = [torch.randn((T, H, 64), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    k = [torch.randn((T, H, 64), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    v = [torch.randn((T, H, 64), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    out_g = torch.empty((T, H, 64), dtype=torch.bfloat16, device=dev)
+    out_f = torch.empty((T, H, 64), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    fb = VGGT_TOKENS * H * 64 * 2
+    # per-frame tables: frame f attends to its own 6 pages (page order of the visible table)
+    upp = -(-VGGT_TOKENS // 256)
+    qo = torch.arange(0, T + 1, VGGT_TOKENS, dtype=torch.int32, device=dev)
+    kv = torch.arange(0, frames * upp + 1, upp, dtype=torch.int32, device=dev)
+    wsb = max(cc.workspace_bytes(T) for cc in caches)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    def one_pass(events=None):
+        tabs = []
+        for l in range(L):
+            cc = caches[l]
+            cc.reset()
+            for f in range(frames):
+                _ok(lb.kvc_append_frame(cc.handle, k[l].data_ptr() + f * fb, v[l].data_ptr() + f * fb, sp), "append")
+            ids, lens = cc.visible_table()
+            tabs.append((torch.from_numpy(ids).to(dev, non_blocking=False), torch.from_numpy(lens).to(dev)))
+            if events is not None:
+                events[4 * l].record()
+            _ok(lb.kvc_attend(cc.handle, q[l].data_ptr(), T, 0.0, out_g.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb,
+                              sp), "attend")
+            if events is not None:
+                events[4 * l + 1].record()
+                events[4 * l + 2].record()
+            paged_attention(q[l], cc.k_pool, cc.v_pool, tabs[l][0], tabs[l][1], qo, kv, VGGT_TOKENS, upp, out=out_f,
+                            lse=None)
+            if events is not None:
+                events[4 * l + 3].record()
+
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_pass()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    fl_g = L * attn_flops(T, T, H)
+    fl_f = L * frames * attn_flops(VGGT_TOKENS, VGGT_TOKENS, H)
+    tf = steps * (fl_g + fl_f) / el / 1e12
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * L)]
+    one_pass(ev)
+    ev[-1].synchronize()
+    tg = sum(ev[4 * l].elapsed_time(ev[4 * l + 1]) for l in range(L)) * 1e-3
+    tfr = sum(ev[4 * l + 2].elapsed_time(ev[4 * l + 3]) for l in range(L)) * 1e-3
+    ach = fl_g / tg / 1e12
+    log(f"[bench] global: {el / steps:.3f} s/pass, {tf:.1f} TFLOP/s overall; global calls {tg / L * 1e3:.2f} ms avg "
+        f"({ach:.1f} TFLOP/s, {ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak); frame calls {tfr / L * 1e3:.2f} ms avg "
+        f"({fl_f / tfr / 1e12:.1f} TFLOP/s)")
+    return {
+        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3, "frames_per_s": steps * frames / el,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+        "config": {"workload": f"vggt_global: 24 layers, 100 frames x 1374 tokens = {T}, 16 heads x 64, bf16, "
+                               "global attention (no mask) + per-frame attention per layer, appends included",
+                   "layers": L, "heads": H, "head_dim": 64, "tokens": T},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "global attention call (attn_bf16_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
+                     "frame_attn_tflops": fl_f / tfr / 1e12},
+    }
+
+
+def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    """A plain device-to-device copy of known size (reference for the FETCH_SIZE/WRITE_SIZE counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", "csrc", "attn_bf16.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic_ratio(name: str):
+    """HBM bytes over algorithmic bytes per call, from a committed counter summary.
+
+    The summary holds lines `kernel_source_sha256_16: <hash>` and
+    `traffic_ratio: <ratio>`.  None if the kernel source changed since the
+    counters were taken (different hash) or the summary is missing.
+    """
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line:
+                    a, b = line.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("kernel_source_sha256_16") != attn_source_hash():
+            return None
+        return float(kv["traffic_ratio"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000, help="frames streamed in the timed region")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps: frames (stream, default 1000), chunk steps (chunked, default 8) or "
+                         "passes (global, default 1)")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stream", choices=["stream"])
+    ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global"])
+    ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=4, help="frames of one layer the oracle times")
+    ap.add_argument("--cpu-sample", type=int, default=40, help="frames of one layer the oracle times")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
@@ -291,7 +495,21 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    res = run_stream(args)
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.steps is None:
+        args.steps = {"stream": 1000, "chunked": 8, "global": 1}[args.workload]
+    if args.workload == "stream":
+        res = run_stream(args)
+        ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md")
+        if ratio is not None:
+            res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
+            res["roofline"]["traffic_ratio"] = ratio
+    elif args.workload == "chunked":
+        res = run_chunked(args)
+    else:
+        res = run_global(args)
     out = {
         "metric": METRIC,
         "value": res["value"],
@@ -304,7 +522,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, 4-frame bank per layer)",
+        "data": "synthetic (seeded N(0,1) Q/K/V drawn on the device)",
         "config": res["config"],
         "frames_per_s": res["frames_per_s"],
         "pct_bf16_mfma_peak": res["pct_bf16_mfma_peak"],
@@ -312,6 +530,7 @@ def main():
     }
     if "cpu_baseline" in res:
         out["cpu_baseline"] = res["cpu_baseline"]
+    out["kernel_source_sha256_16"] = attn_source_hash()
     print(json.dumps(out), flush=True)
 
 
