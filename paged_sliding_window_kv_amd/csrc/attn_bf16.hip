@@ -318,12 +318,9 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
     else
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     __builtin_amdgcn_s_barrier();
-    // The previous pair's stages are free now: refill them.
-    for (int s = 0; s < 2 && lc.e < ee; ++s) {
-      issue(lc, ni % STAGES);
-      cursor_next(src, ee, lc);
-      ++ni;
-    }
+    // The previous pair's stages are free now; they are refilled after this
+    // pair's products (below), so that the waves do not all queue their loads
+    // on the vector-memory pipe at the same moment.
     Cursor cb = cc;
     const int nka = min(KT, cc.len - cc.kt * KT);
     int nkb = 0;
@@ -414,9 +411,10 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
       };
       floatx16 a0, a1, b0, b1;
       if (two && nka == KT && nkb == KT) {
-        // Full pair: one straight-line block.  Waves w and w+4 share a SIMD;
-        // the upper half takes the pair in the opposite order so that one
-        // wave's softmax arithmetic tends to run under the other's products.
+        // Full pair: one straight-line block with a single softmax update for
+        // all 128 keys.  Waves w and w+4 share a SIMD; the upper half takes the
+        // pair in the opposite order so that one wave's softmax arithmetic
+        // tends to run under the other's products.
         const bool rev = (wave & 4) != 0;
         const uint16_t* k1 = rev ? lkb : lka;
         const uint16_t* k2 = rev ? lka : lkb;
@@ -426,9 +424,28 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
         qk(k1, a0, a1);
         qk(k2, b0, b1);
         __builtin_amdgcn_s_setprio(0);
-        soft(a0, a1, KT, true);
+        const float mx = pair_max(fmaxf(tile_max(a0, a1), tile_max(b0, b1))) * sl2;
+        if (__any(mx > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            o0[r] *= alpha;
+            o1[r] *= alpha;
+          }
+        }
+        const float nm = -m_run;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          a0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a0[r], sl2, nm));
+          a1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[r], sl2, nm));
+          b0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(b0[r], sl2, nm));
+          b1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(b1[r], sl2, nm));
+        }
+        l_run += tile_sum(a0, a1) + tile_sum(b0, b1);
         pv(a0, a1, v1);
-        soft(b0, b1, KT, true);
         pv(b0, b1, v2);
       } else {
         qk(lka, a0, a1);
@@ -489,6 +506,11 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
         }
         __builtin_amdgcn_s_setprio(0);
       }
+    }
+    for (int s = 0; s < 2 && lc.e < ee; ++s) {
+      issue(lc, ni % STAGES);
+      cursor_next(src, ee, lc);
+      ++ni;
     }
     nc += two ? 2 : 1;
     if (two) cc = cb;
