@@ -12,6 +12,8 @@ Inputs are seeded synthetic N(0,1) tensors, resident in HBM before timing.
 Other workloads (--workload): "chunked" is VGGT-style chunked global attention
 (8-frame chunks of 1374 tokens, window of 4 chunks).  "global" is full global
 attention over 100 frames x 1374 tokens followed by per-frame attention.
+"stream_batched" runs --batch LingBot streams side by side: per layer and frame,
+each stream appends its frame and one launch serves all streams' attention.
 """
 from __future__ import annotations
 
@@ -291,6 +293,100 @@ def run_stream(args) -> dict:
     return res
 
 
+def run_stream_batched(args) -> dict:
+    """B LingBot-shaped streams; per layer and frame, B appends then one batched attention launch."""
+    import torch
+    from paged_sliding_window_kv_amd import attend_batch_workspace_bytes, lib, shared_pool_caches
+    c = STREAM
+    B, L, frames = args.batch, c["layers"], args.steps
+    tok = c["patch"] + c["special"]
+    log(f"[bench] stream_batched: {B} streams x {L} layers x {frames} frames, warmup {args.warmup}")
+    dev = torch.device("cuda:0")
+    lb = lib()
+    kw = dict(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], dtype="bf16", patch_tokens=c["patch"],
+              special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
+              max_units=max(frames, args.warmup, 64))
+    layers = [shared_pool_caches(B, dev, **kw) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    bank = 4
+    shp = (bank, B * tok, c["heads"], c["d"])
+    qs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    ks = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    vs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    out = torch.empty((B * tok, c["heads"], c["d"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B * tok, c["heads"]), dtype=torch.float32, device=dev)
+    qo = np.arange(0, B * tok + 1, tok, dtype=np.int32)
+    qop = qo.ctypes.data_as(C.POINTER(C.c_int32))
+    # largest workspace over the stream: the batch at its longest tables
+    probe = shared_pool_caches(B, dev, **kw)
+    for _ in range(min(frames, c["scale"] + c["window"] + 1)):
+        for cc in probe:
+            cc.append(ks[0][0, :tok], vs[0][0, :tok])
+    wsb = attend_batch_workspace_bytes(probe, qo) * 2
+    del probe
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    fb = tok * c["heads"] * c["d"] * 2
+    handles = [(C.c_void_p * B)(*[cc.handle.value for cc in layer]) for layer in layers]
+    hlist = [[cc.handle for cc in layer] for layer in layers]
+
+    def step(t, ev=None):
+        b = t % bank
+        for l in range(L):
+            kb, vb = ks[l].data_ptr() + b * B * fb, vs[l].data_ptr() + b * B * fb
+            for i in range(B):
+                _ok(lb.kvc_append_frame(hlist[l][i], kb + i * fb, vb + i * fb, sp), "append")
+        if ev is not None:
+            ev[0].record()
+        for l in range(L):
+            _ok(lb.kvc_attend_batch(handles[l], B, qs[l].data_ptr() + b * B * fb, qop, 0.0, out.data_ptr(),
+                                    lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend_batch")
+        if ev is not None:
+            ev[1].record()
+
+    def reset():
+        for layer in layers:
+            for cc in layer:
+                cc.reset()
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(frames):
+        step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    flops = sum(B * L * attn_flops(tok, stream_lk(t), c["heads"]) for t in range(frames))
+    byts = sum(B * L * attn_bytes(tok, stream_lk(t), c["heads"]) for t in range(frames))
+    reset()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    att = 0.0
+    for t in range(frames):
+        step(t, ev)
+        ev[1].synchronize()
+        att += ev[0].elapsed_time(ev[1]) * 1e-3
+    n = frames * L
+    tf = flops / el / 1e12
+    ach = byts / att / 1e9
+    log(f"[bench] stream_batched: {el / frames * 1e3:.2f} ms per frame step, {B * frames / el:.1f} frames/s over "
+        f"{B} streams, {tf:.1f} TFLOP/s; batched calls {att / n * 1e6:.1f} us avg ({ach:.0f} GB/s, "
+        f"{flops / att / 1e12:.1f} TFLOP/s)")
+    return {
+        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / frames * 1e3, "frames_per_s": B * frames / el,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+        "config": {"workload": f"lingbot_stream_batched: {B} streams x 24 layer caches, 16 heads x 64, bf16, "
+                               f"262 queries/stream/step, {frames} frames, one attention launch per layer and frame",
+                   "streams": B, "layers": L, "frames": frames},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                     "traffic": None, "kernel": "batched attention call (attn_bf16_kernel + attn_merge_kernel)",
+                     "avg_call_us": att / n * 1e6, "calls": n, "attn_tflops": flops / att / 1e12},
+    }
+
+
 # ----------------------------------------------------------------------------
 # VGGT-style chunked global attention and full global + frame attention
 # ----------------------------------------------------------------------------
@@ -500,7 +596,9 @@ def main():
                     help="timed steps: frames (stream, default 1000), chunk steps (chunked, default 8) or "
                          "passes (global, default 1)")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global"])
+    ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global", "stream_batched"])
+    ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
+                    "the 1000-frame tables within one launch)")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=40, help="frames of one layer the oracle times")
@@ -517,7 +615,7 @@ def main():
         copy_probe()
         return
     if args.steps is None:
-        args.steps = {"stream": 1000, "chunked": 8, "global": 1}[args.workload]
+        args.steps = {"stream": 1000, "chunked": 8, "global": 1, "stream_batched": 1000}[args.workload]
     if args.workload == "stream":
         res = run_stream(args)
         ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md")
@@ -526,6 +624,8 @@ def main():
             res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "chunked":
         res = run_chunked(args)
+    elif args.workload == "stream_batched":
+        res = run_stream_batched(args)
     else:
         res = run_global(args)
     out = {

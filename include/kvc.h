@@ -239,6 +239,34 @@ int kvc_attend(const kvc_t* cache, const void* q, int32_t num_q, float sm_scale,
                void* workspace, size_t workspace_bytes, kvc_stream_t stream);
 int kvc_attend_workspace_size(const kvc_t* cache, int32_t num_q, size_t* bytes);
 
+/* One attention step of several caches in one launch: the scheduler of the
+ * vLLM-Omni RFC #2727 (sections 3.2-3.3) batches the current chunks of
+ * several requests; here every cache is one request or stream.  Cache i's
+ * queries are rows qo_indptr[i] .. qo_indptr[i+1]-1 of q, and they attend to
+ * cache i's visible table exactly as in kvc_attend.
+ *
+ * caches: num_caches handles (1..16) with equal num_heads, head_dim,
+ * page_size and dtype.  Their pools must lie in one shared K allocation and
+ * one shared V allocation: each cache's K pool starts a whole number of pages
+ * after the lowest K pool pointer of the batch, and its V pool the same
+ * number of pages after the lowest V pool pointer (pools handed to
+ * kvc_create as page-aligned slices of two big buffers).  The combined tables
+ * travel in the launch arguments: at most 640 entries in total, else
+ * KVC_ERR_UNSUPPORTED (split the batch).
+ * qo_indptr: host array of num_caches + 1 non-decreasing offsets, first 0.
+ * q, o: device [qo_indptr[num_caches]][H][d] in the cache dtype; lse: device
+ * [..][H] fp32 or NULL; sm_scale <= 0 means 1/sqrt(d).  workspace: device
+ * scratch of kvc_attend_batch_workspace_size bytes for the same arguments
+ * (it depends on the caches' current table lengths).
+ * Errors: KVC_ERR_INVALID_ARGUMENT for mismatched configs, pools outside a
+ * shared allocation, host-only caches or bad offsets; nothing is launched
+ * then.  The caches are not modified. */
+int kvc_attend_batch(const kvc_t* const* caches, int32_t num_caches, const void* q, const int32_t* qo_indptr,
+                     float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     kvc_stream_t stream);
+int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_caches, const int32_t* qo_indptr,
+                                    size_t* bytes);
+
 const char* kvc_strerror(int status);
 const char* kvc_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */

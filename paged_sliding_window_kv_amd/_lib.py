@@ -29,9 +29,11 @@ EXPORTED = (
     "kvc_required_pages", "kvc_pool_bytes", "kvc_create", "kvc_destroy", "kvc_append_frame",
     "kvc_rollback_last_frame", "kvc_reset", "kvc_build_visible_table", "kvc_get_state",
     "paged_attn_workspace_size", "paged_attn_num_splits", "paged_attn_fwd", "paged_attn_merge",
-    "kvc_attend", "kvc_attend_workspace_size", "kvc_strerror", "kvc_last_error", "kvc_version",
+    "kvc_attend", "kvc_attend_workspace_size", "kvc_attend_batch", "kvc_attend_batch_workspace_size",
+    "kvc_strerror", "kvc_last_error", "kvc_version",
 )
 MAX_INLINE_PAGES = 640
+MAX_BATCH_CACHES = 16
 
 
 class KvcConfig(C.Structure):
@@ -122,6 +124,8 @@ def _declare(lib):
         "paged_attn_merge": (C.c_int, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "kvc_attend": (C.c_int, [vp, vp, i32, C.c_float, vp, vp, vp, C.c_size_t, vp]),
         "kvc_attend_workspace_size": (C.c_int, [vp, i32, C.POINTER(C.c_size_t)]),
+        "kvc_attend_batch": (C.c_int, [C.POINTER(vp), i32, vp, i32p, C.c_float, vp, vp, vp, C.c_size_t, vp]),
+        "kvc_attend_batch_workspace_size": (C.c_int, [C.POINTER(vp), i32, i32p, C.POINTER(C.c_size_t)]),
         "kvc_strerror": (C.c_char_p, [C.c_int]),
         "kvc_last_error": (C.c_char_p, []),
         "kvc_version": (C.c_int, []),

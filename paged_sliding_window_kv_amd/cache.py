@@ -45,7 +45,7 @@ class KvCache:
     def __init__(self, num_heads: int, head_dim: int = 64, page_size: int = 256, dtype: str = "bf16",
                  patch_tokens: int = 256, special_tokens: int = 6, num_scale_units: int = 8,
                  window_units: int = 64, special_packing: str = "frame_aligned", max_units: int = 1000,
-                 num_pages: int = 0, device=None):
+                 num_pages: int = 0, device=None, pools=None):
         self.cfg = L.KvcConfig(num_heads, head_dim, page_size, _DTYPES[dtype], patch_tokens, special_tokens,
                                num_scale_units, window_units, _PACKING[special_packing], max_units, num_pages)
         self.dtype = dtype
@@ -59,7 +59,20 @@ class KvCache:
         self.num_pages = n.value
         self.device = device
         self.k_pool = self.v_pool = None
-        if device is not None:
+        if pools is not None:
+            # caller-owned pool tensors (e.g. page slices of a pool shared by a batch)
+            k_pool, v_pool = pools
+            want_k = (self.num_pages, num_heads, page_size, head_dim)
+            want_v = (self.num_pages, num_heads, head_dim, page_size)
+            if tuple(k_pool.shape) != want_k or tuple(v_pool.shape) != want_v:
+                raise ValueError(f"pools must have shapes {want_k} and {want_v}")
+            if not (k_pool.is_contiguous() and v_pool.is_contiguous()):
+                raise ValueError("pools must be contiguous")
+            if k_pool.dtype != torch_dtype(dtype) or v_pool.dtype != torch_dtype(dtype):
+                raise ValueError(f"pools must be {dtype}")
+            self.k_pool, self.v_pool = k_pool, v_pool
+            self.device = k_pool.device
+        elif device is not None:
             t = _torch()
             td = torch_dtype(dtype)
             self.k_pool = t.empty((self.num_pages, num_heads, page_size, head_dim), dtype=td, device=device)
@@ -193,3 +206,69 @@ class KvCache:
         return paged_attention(q, self.k_pool, self.v_pool, page_ids, page_lens, qo, kv,
                                max_qo_len=q.shape[0], max_kv_pages=len(ids), out=out, lse=lse,
                                sm_scale=sm_scale, num_splits=num_splits, stream=stream)
+
+
+def shared_pool_caches(count: int, device, **cfg) -> list:
+    """`count` caches with one config whose pools are page slices of one shared K and one shared V tensor.
+
+    Such caches can attend together in one launch (attend_batch).  Keyword
+    arguments are KvCache's; num_pages per cache is derived from the config
+    unless given.
+    """
+    t = _torch()
+    probe = KvCache(**cfg)  # host-only: page count and shapes
+    n, H, P, d = probe.num_pages, probe.num_heads, probe.page_size, probe.head_dim
+    td = torch_dtype(probe.dtype)
+    probe.close()
+    k_all = t.empty((count * n, H, P, d), dtype=td, device=device)
+    v_all = t.empty((count * n, H, d, P), dtype=td, device=device)
+    caches = []
+    for i in range(count):
+        c = dict(cfg)
+        c["num_pages"] = n
+        caches.append(KvCache(pools=(k_all[i * n:(i + 1) * n], v_all[i * n:(i + 1) * n]), **c))
+    return caches
+
+
+def attend_batch_workspace_bytes(caches, qo_indptr) -> int:
+    hs = (C.c_void_p * len(caches))(*[c.handle.value for c in caches])
+    qo = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    n = C.c_size_t()
+    L.check(L.lib().kvc_attend_batch_workspace_size(hs, len(caches), qo.ctypes.data_as(C.POINTER(C.c_int32)),
+                                                    C.byref(n)), "kvc_attend_batch_workspace_size")
+    return n.value
+
+
+def attend_batch(caches, q, qo_indptr, out=None, lse=None, sm_scale: Optional[float] = None, workspace=None,
+                 stream: Optional[int] = None):
+    """One launch of attention for several caches (kvc_attend_batch).
+
+    q: [total, H, d] device tensor; rows qo_indptr[i] .. qo_indptr[i+1]-1 belong
+    to caches[i].  The caches must share pools (shared_pool_caches).  Returns
+    (out, lse).
+    """
+    t = _torch()
+    c0 = caches[0]
+    dev = c0.k_pool.device
+    qo = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    if len(qo) != len(caches) + 1 or int(qo[-1]) != q.shape[0]:
+        raise ValueError("qo_indptr must have len(caches) + 1 entries ending at q.shape[0]")
+    if tuple(q.shape[1:]) != (c0.num_heads, c0.head_dim) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total, H, d] tensor")
+    if q.dtype != torch_dtype(c0.dtype) or q.device != dev:
+        raise ValueError(f"q must be {c0.dtype} on {dev}")
+    if out is None:
+        out = t.empty_like(q)
+    if lse is None:
+        lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
+    need = attend_batch_workspace_bytes(caches, qo)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = t.empty(need, dtype=t.uint8, device=dev)
+    wp = workspace.data_ptr() if need else None
+    wb = workspace.numel() * workspace.element_size() if need else 0
+    s = current_stream_ptr(dev) if stream is None else stream
+    hs = (C.c_void_p * len(caches))(*[c.handle.value for c in caches])
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    L.check(L.lib().kvc_attend_batch(hs, len(caches), q.data_ptr(), qo.ctypes.data_as(C.POINTER(C.c_int32)), scale,
+                                     out.data_ptr(), lse.data_ptr(), wp, wb, s), "kvc_attend_batch")
+    return out, lse

@@ -381,8 +381,131 @@ int kvc_attend(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, voi
   int splits = 1;
   if (int s = setup_attn(a, pi.base, &splits)) return s;
   pi.num_entries = n;
+  pi.qo[0] = 0;
+  pi.qo[1] = num_q;
+  pi.kv[0] = 0;
+  pi.kv[1] = n;
   for (int32_t i = 0; i < n; ++i)
     pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
+  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks a batch of caches for kvc_attend_batch and derives its launch
+// arguments: every cache's pool offset (whole pages from the lowest pool
+// pointer of the batch, the same for K and V) and the combined sizes.
+int batch_args(const kvc_t* const* caches, int32_t n, const int32_t* qo, float sm_scale, paged_attn_args* a,
+               int32_t* page_off) {
+  if (!caches || n <= 0 || !qo) return fail(KVC_ERR_INVALID_ARGUMENT, "bad batch");
+  if (n > kvc::kMaxInlineSeqs) return fail(KVC_ERR_UNSUPPORTED, "batch of %d caches (at most %d)", n, kvc::kMaxInlineSeqs);
+  if (!(sm_scale >= 0.f) || !std::isfinite(sm_scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "bad sm_scale");
+  if (qo[0] != 0) return fail(KVC_ERR_INVALID_ARGUMENT, "qo_indptr[0] must be 0");
+  const kvc_t* c0 = caches[0];
+  if (!c0) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL cache in batch");
+  const kvc_config& f = c0->pc.config();
+  const char* base_k = nullptr;
+  const char* base_v = nullptr;
+  int32_t entries = 0, max_q = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const kvc_t* c = caches[i];
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL cache in batch");
+    if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache %d has no device pools", i);
+    const kvc_config& g = c->pc.config();
+    if (g.num_heads != f.num_heads || g.head_dim != f.head_dim || g.page_size != f.page_size || g.dtype != f.dtype)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "cache %d: heads, head_dim, page_size and dtype must match the batch", i);
+    if (qo[i + 1] < qo[i]) return fail(KVC_ERR_INVALID_ARGUMENT, "qo_indptr must be non-decreasing");
+    max_q = std::max(max_q, qo[i + 1] - qo[i]);
+    entries += c->pc.visible_count();
+    const char* k = static_cast<const char*>(c->k_pool);
+    const char* v = static_cast<const char*>(c->v_pool);
+    if (!base_k || k < base_k) base_k = k;
+    if (!base_v || v < base_v) base_v = v;
+  }
+  if (entries > kvc::kMaxInlinePages)
+    return fail(KVC_ERR_UNSUPPORTED, "batch has %d table entries (at most %d)", entries, kvc::kMaxInlinePages);
+  const size_t page_bytes = static_cast<size_t>(f.num_heads) * f.page_size * f.head_dim * elem_size(f.dtype);
+  int64_t pool_pages = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const size_t dk = static_cast<size_t>(static_cast<const char*>(caches[i]->k_pool) - base_k);
+    const size_t dv = static_cast<size_t>(static_cast<const char*>(caches[i]->v_pool) - base_v);
+    if (dk % page_bytes != 0 || dk != dv)
+      return fail(KVC_ERR_INVALID_ARGUMENT,
+                  "cache %d: pools must sit whole pages into one shared K and one shared V allocation, "
+                  "at the same page offset", i);
+    const int64_t off = static_cast<int64_t>(dk / page_bytes);
+    pool_pages = std::max<int64_t>(pool_pages, off + caches[i]->pc.num_pages());
+    if (pool_pages > kvc::kInlineMaxPid + 1) return fail(KVC_ERR_UNSUPPORTED, "shared pool too large for inline tables");
+    page_off[i] = static_cast<int32_t>(off);
+  }
+  if (f.page_size > 4095) return fail(KVC_ERR_UNSUPPORTED, "page size too large for inline tables");
+  *a = paged_attn_args{};
+  a->dtype = f.dtype;
+  a->num_heads = f.num_heads;
+  a->head_dim = f.head_dim;
+  a->page_size = f.page_size;
+  a->sm_scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt(static_cast<float>(f.head_dim));
+  a->num_seqs = n;
+  a->total_q = qo[n];
+  a->max_qo_len = max_q;
+  int32_t max_pages = 0;
+  for (int32_t i = 0; i < n; ++i) max_pages = std::max(max_pages, caches[i]->pc.visible_count());
+  a->max_kv_pages = max_pages;
+  a->num_pool_pages = static_cast<int32_t>(pool_pages);
+  a->num_splits = 0;
+  a->k_pool = base_k;
+  a->v_pool = base_v;
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_caches, const int32_t* qo_indptr,
+                                    size_t* bytes) {
+  if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
+  paged_attn_args a;
+  int32_t off[kvc::kMaxInlineSeqs];
+  if (int s = batch_args(caches, num_caches, qo_indptr, 0.f, &a, off)) return s;
+  if (int s = check_attn_args(&a)) return s;
+  *bytes = workspace_for(a, choose_splits(a));
+  return KVC_OK;
+}
+
+int kvc_attend_batch(const kvc_t* const* caches, int32_t num_caches, const void* q, const int32_t* qo_indptr,
+                     float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                     kvc_stream_t stream) {
+  paged_attn_args a;
+  int32_t off[kvc::kMaxInlineSeqs];
+  if (int s = batch_args(caches, num_caches, qo_indptr, sm_scale, &a, off)) return s;
+  if (a.total_q == 0) return KVC_OK;
+  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (int s = check_attn_args(&a)) return s;
+  static thread_local kvc::AttnParamsInline pi;
+  int splits = 1;
+  if (int s = setup_attn(a, pi.base, &splits)) return s;
+  int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
+  int32_t e = 0;
+  pi.qo[0] = 0;
+  pi.kv[0] = 0;
+  for (int32_t i = 0; i < num_caches; ++i) {
+    const int32_t m = caches[i]->pc.visible_count();
+    caches[i]->pc.visible_table(ids + e, lens + e);
+    for (int32_t j = e; j < e + m; ++j)
+      pi.entries[j] = static_cast<uint32_t>(ids[j] + off[i]) | (static_cast<uint32_t>(lens[j]) << kvc::kInlinePidBits);
+    e += m;
+    pi.qo[i + 1] = qo_indptr[i + 1];
+    pi.kv[i + 1] = e;
+  }
+  pi.num_entries = e;
   return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
 }
 

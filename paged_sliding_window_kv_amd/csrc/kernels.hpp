@@ -67,18 +67,21 @@ struct AttnParams {
   float scale_log2;       // sm_scale * log2(e)
 };
 
-// Most table entries passed by value in the kernel arguments (single
-// sequence).  Each entry packs page id (low 20 bits) and valid length (high
-// 12 bits); with the parameters above the argument block stays under 3 KiB.
+// Most table entries and sequences passed by value in the kernel arguments.
+// Each entry packs page id (low 20 bits) and valid length (high 12 bits);
+// with the parameters above the argument block stays under 3 KiB.
 constexpr int kMaxInlinePages = 640;
+constexpr int kMaxInlineSeqs = 16;
 constexpr int kInlinePidBits = 20;
 constexpr int kInlineMaxPid = (1 << kInlinePidBits) - 1;
 
-// Paged attention of one sequence whose table travels in the kernel
-// arguments: queries [0, total_q), entries [0, num_entries).
+// Paged attention whose tables travel in the kernel arguments: sequence s
+// has queries [qo[s], qo[s+1]) and entries [kv[s], kv[s+1]) of `entries`.
 struct AttnParamsInline {
   AttnParams base;
   int32_t num_entries;
+  int32_t qo[kMaxInlineSeqs + 1];
+  int32_t kv[kMaxInlineSeqs + 1];
   uint32_t entries[kMaxInlinePages];
 };
 
@@ -100,11 +103,11 @@ __device__ __forceinline__ void attn_seq(const AttnParams& p, int seq, int& q0, 
   e0 = ld_const(p.kv_indptr, seq);
   en = ld_const(p.kv_indptr, seq + 1) - e0;
 }
-__device__ __forceinline__ void attn_seq(const AttnParamsInline& p, int, int& q0, int& qn, int& e0, int& en) {
-  q0 = 0;
-  qn = p.base.total_q;
-  e0 = 0;
-  en = p.num_entries;
+__device__ __forceinline__ void attn_seq(const AttnParamsInline& p, int seq, int& q0, int& qn, int& e0, int& en) {
+  q0 = p.qo[seq];
+  qn = p.qo[seq + 1] - q0;
+  e0 = p.kv[seq];
+  en = p.kv[seq + 1] - e0;
 }
 
 // Page id and valid length of table entry e; invalid ids and lengths give 0.

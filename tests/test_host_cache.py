@@ -175,3 +175,64 @@ def test_split_choice_and_workspace():
     # many query tiles: no split
     a.num_splits, a.total_q, a.max_qo_len, a.max_kv_pages = 0, 10992, 10992, 172
     assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 1
+
+
+def test_attend_batch_argument_checks():
+    """kvc_attend_batch validates the batch on the host (no pool memory is touched here)."""
+    lib = L.lib()
+    H, P, d = 2, 256, 64
+    cfg = L.KvcConfig(H, d, P, 0, 256, 6, 1, 2, 0, 10, 0)
+    n = C.c_int32()
+    assert lib.kvc_required_pages(C.byref(cfg), C.byref(n)) == 0
+    page_bytes = H * P * d * 2
+    base_k, base_v = 1 << 32, 1 << 33          # placeholder addresses, never dereferenced
+    hs = []
+    for i in range(3):
+        h = C.c_void_p()
+        assert lib.kvc_create(C.byref(cfg), C.c_void_p(base_k + i * n.value * page_bytes),
+                              C.c_void_p(base_v + i * n.value * page_bytes), C.byref(h)) == 0
+        hs.append(h)
+    for h in hs:
+        assert lib.kvc_append_frame(h, None, None, None) in (0, L.KVC_ERR_INVALID_ARGUMENT)
+    arr = (C.c_void_p * 3)(*[h.value for h in hs])
+    qo = (C.c_int32 * 4)(0, 262, 262, 400)
+    sz = C.c_size_t()
+    assert lib.kvc_attend_batch_workspace_size(arr, 3, qo, C.byref(sz)) == 0
+    # bad offsets, counts and sizes
+    assert lib.kvc_attend_batch_workspace_size(arr, 0, qo, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_attend_batch_workspace_size(arr, 17, qo, C.byref(sz)) == L.KVC_ERR_UNSUPPORTED
+    bad_qo = (C.c_int32 * 4)(1, 262, 262, 400)
+    assert lib.kvc_attend_batch_workspace_size(arr, 3, bad_qo, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    dec_qo = (C.c_int32 * 4)(0, 262, 100, 400)
+    assert lib.kvc_attend_batch_workspace_size(arr, 3, dec_qo, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    # NULL q with a valid batch is rejected before anything is launched
+    assert lib.kvc_attend_batch(arr, 3, None, qo, 0.0, None, None, None, 0, None) == L.KVC_ERR_INVALID_ARGUMENT
+    # a pool that is not a whole number of pages into the shared allocation
+    odd = C.c_void_p()
+    assert lib.kvc_create(C.byref(cfg), C.c_void_p(base_k + 3 * n.value * page_bytes + 128),
+                          C.c_void_p(base_v + 3 * n.value * page_bytes + 128), C.byref(odd)) == 0
+    arr2 = (C.c_void_p * 2)(hs[0].value, odd.value)
+    qo2 = (C.c_int32 * 3)(0, 10, 20)
+    assert lib.kvc_attend_batch_workspace_size(arr2, 2, qo2, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    assert b"whole pages" in lib.kvc_last_error()
+    # K and V at different page offsets
+    skew = C.c_void_p()
+    assert lib.kvc_create(C.byref(cfg), C.c_void_p(base_k + 3 * n.value * page_bytes),
+                          C.c_void_p(base_v + 4 * n.value * page_bytes), C.byref(skew)) == 0
+    arr3 = (C.c_void_p * 2)(hs[0].value, skew.value)
+    assert lib.kvc_attend_batch_workspace_size(arr3, 2, qo2, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    # a different head count
+    cfg4 = L.KvcConfig(4, d, P, 0, 256, 6, 1, 2, 0, 10, 0)
+    other = C.c_void_p()
+    assert lib.kvc_create(C.byref(cfg4), C.c_void_p(base_k + 8 * n.value * page_bytes),
+                          C.c_void_p(base_v + 8 * n.value * page_bytes), C.byref(other)) == 0
+    arr4 = (C.c_void_p * 2)(hs[0].value, other.value)
+    assert lib.kvc_attend_batch_workspace_size(arr4, 2, qo2, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    # host-only caches cannot attend
+    ho = C.c_void_p()
+    assert lib.kvc_create(C.byref(cfg), None, None, C.byref(ho)) == 0
+    arr5 = (C.c_void_p * 1)(ho.value)
+    qo1 = (C.c_int32 * 2)(0, 5)
+    assert lib.kvc_attend_batch_workspace_size(arr5, 1, qo1, C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    for h in hs + [odd, skew, other, ho]:
+        assert lib.kvc_destroy(h) == 0
