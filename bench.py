@@ -421,14 +421,21 @@ def run_chunked(args) -> dict:
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
 
+    kr = args.keep_ratio
+
     def step(i, events=None):
         b = i % bank
         for l in range(L):
             _ok(lb.kvc_append_frame(caches[l].handle, ks[l][b].data_ptr(), vs[l][b].data_ptr(), sp), "append")
             if events is not None:
                 events[2 * l].record()
-            _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), tokens, 0.0, out.data_ptr(), lse.data_ptr(),
-                              ws.data_ptr(), wsb, sp), "attend")
+            if kr < 1.0:
+                # AVGGT-style: each layer its own random page subset (seed = layer)
+                _ok(lb.kvc_attend_subset(caches[l].handle, kr, l, 0, 0, qs[l][b].data_ptr(), tokens, 0.0,
+                                         out.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend_subset")
+            else:
+                _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), tokens, 0.0, out.data_ptr(),
+                                  lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend")
             if events is not None:
                 events[2 * l + 1].record()
 
@@ -441,7 +448,13 @@ def run_chunked(args) -> dict:
         step(warm + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    flops = steps * L * attn_flops(tokens, lk, c["heads"])
+    if kr < 1.0:
+        # keys actually attended per layer: the subset keeps the same table positions every steady-state step
+        lks = [int(caches[l].subset_table(kr, l)[1].sum()) for l in range(L)]
+        flops = steps * sum(attn_flops(tokens, x, c["heads"]) for x in lks)
+        lk = sum(lks) / L
+    else:
+        flops = steps * L * attn_flops(tokens, lk, c["heads"])
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
     att = 0.0
     for i in range(steps):
@@ -458,8 +471,11 @@ def run_chunked(args) -> dict:
         "frames_per_s": steps * c["frames_per_chunk"] / el,
         "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
         "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, bf16, chunks of 8 x 1374 = {tokens} "
-                               f"tokens, window 4 chunks ({lk} visible keys), {steps} timed chunk steps",
-                   "layers": L, "heads": 16, "head_dim": 64, "chunk_tokens": tokens, "visible_tokens": lk},
+                               f"tokens, window 4 chunks ({W * tokens} visible keys)"
+                               + (f", per-layer page subsets keeping {kr} ({lk:.0f} keys attended)" if kr < 1.0 else "")
+                               + f", {steps} timed chunk steps",
+                   "layers": L, "heads": 16, "head_dim": 64, "chunk_tokens": tokens, "visible_tokens": W * tokens,
+                   "keep_ratio": kr, "attended_tokens": lk},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": "paged attention call (attn_bf16_kernel)", "avg_call_us": att / n * 1e6,
@@ -599,6 +615,8 @@ def main():
     ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global", "stream_batched"])
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
+    ap.add_argument("--keep-ratio", type=float, default=1.0,
+                    help="chunked: attend to a per-layer random page subset keeping this fraction (AVGGT-style)")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=40, help="frames of one layer the oracle times")

@@ -239,6 +239,28 @@ int kvc_attend(const kvc_t* cache, const void* q, int32_t num_q, float sm_scale,
                void* workspace, size_t workspace_bytes, kvc_stream_t stream);
 int kvc_attend_workspace_size(const kvc_t* cache, int32_t num_q, size_t* bytes);
 
+/* Page-subset table ("vLLM-Omni RFC #2727: Reconstruction Engine", section
+ * 3.4, KV compression: AVGGT lets each layer attend to its own random subset
+ * of the KV).  Sampling is per page of the visible table.  The first
+ * keep_first and the last keep_last entries are always kept (e.g. scale
+ * pages as anchors, special pages, the current unit).  Of the n entries in
+ * between, ceil(keep_ratio * n) are kept: those with the smallest
+ * splitmix64_i(seed), the i-th output of splitmix64 seeded with `seed`
+ * (Steele, Lea, Flood 2014), where i is the entry's index in the visible
+ * table; ties would go to the lower index.  Kept entries stay in table order.
+ * Pass a different seed per layer for AVGGT's per-layer subsets.
+ * keep_ratio in (0, 1]; 1 gives the full visible table.  Output and errors
+ * as kvc_build_visible_table: *num_pages is set even when capacity is too
+ * small (KVC_ERR_BUFFER_TOO_SMALL). */
+int kvc_build_subset_table(const kvc_t* cache, float keep_ratio, uint64_t seed, int32_t keep_first,
+                           int32_t keep_last, int32_t* page_ids, int32_t* page_lens, int32_t capacity,
+                           int32_t* num_pages);
+/* kvc_attend over that subset table instead of the full visible table (same
+ * arguments, workspace of kvc_attend_workspace_size bytes). */
+int kvc_attend_subset(const kvc_t* cache, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
+                      const void* q, int32_t num_q, float sm_scale, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, kvc_stream_t stream);
+
 /* One attention step of several caches in one launch: the scheduler of the
  * vLLM-Omni RFC #2727 (sections 3.2-3.3) batches the current chunks of
  * several requests; here every cache is one request or stream.  Cache i's

@@ -10,6 +10,8 @@ Contents
               sliding window, special), the visible page table and the
               single-level rollback, exactly as written in the readings of
               the pages listed in the module docstring.
+  subset      page-subset visible tables (per-layer random page sampling)
+              with the splitmix64 generator written out.
   attention   softmax attention in float64 over gathered pages, a dense
               reference over tokens selected straight from the frame history,
               a brute-force scalar version for tiny shapes, and the merge of
@@ -28,3 +30,4 @@ from .attention import (  # noqa: F401
     attention_f64, brute_attention, merge_partials, bf16_bits_to_f64, to_f64,
     dense_history_attention,
 )
+from .subset import splitmix64, subset_table, subset_keep_count  # noqa: F401,E402

@@ -30,6 +30,7 @@ EXPORTED = (
     "kvc_rollback_last_frame", "kvc_reset", "kvc_build_visible_table", "kvc_get_state",
     "paged_attn_workspace_size", "paged_attn_num_splits", "paged_attn_fwd", "paged_attn_merge",
     "kvc_attend", "kvc_attend_workspace_size", "kvc_attend_batch", "kvc_attend_batch_workspace_size",
+    "kvc_build_subset_table", "kvc_attend_subset",
     "kvc_strerror", "kvc_last_error", "kvc_version",
 )
 MAX_INLINE_PAGES = 640
@@ -124,6 +125,9 @@ def _declare(lib):
         "paged_attn_merge": (C.c_int, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "kvc_attend": (C.c_int, [vp, vp, i32, C.c_float, vp, vp, vp, C.c_size_t, vp]),
         "kvc_attend_workspace_size": (C.c_int, [vp, i32, C.POINTER(C.c_size_t)]),
+        "kvc_build_subset_table": (C.c_int, [vp, C.c_float, C.c_uint64, i32, i32, i32p, i32p, i32, i32p]),
+        "kvc_attend_subset": (C.c_int, [vp, C.c_float, C.c_uint64, i32, i32, vp, i32, C.c_float, vp, vp, vp,
+                                        C.c_size_t, vp]),
         "kvc_attend_batch": (C.c_int, [C.POINTER(vp), i32, vp, i32p, C.c_float, vp, vp, vp, C.c_size_t, vp]),
         "kvc_attend_batch_workspace_size": (C.c_int, [C.POINTER(vp), i32, i32p, C.POINTER(C.c_size_t)]),
         "kvc_strerror": (C.c_char_p, [C.c_int]),

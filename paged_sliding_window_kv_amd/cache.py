@@ -140,6 +140,17 @@ class KvCache:
                 "kvc_build_visible_table")
         return self._ids[:n.value].copy(), self._lens[:n.value].copy()
 
+    def subset_table(self, keep_ratio: float, seed: int, keep_first: int = 0,
+                     keep_last: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Page-subset of the visible table (kvc_build_subset_table)."""
+        n = C.c_int32()
+        ip = self._ids.ctypes.data_as(C.POINTER(C.c_int32))
+        lp = self._lens.ctypes.data_as(C.POINTER(C.c_int32))
+        L.check(L.lib().kvc_build_subset_table(self._h, float(keep_ratio), int(seed) & (2**64 - 1), keep_first,
+                                               keep_last, ip, lp, self.num_pages, C.byref(n)),
+                "kvc_build_subset_table")
+        return self._ids[:n.value].copy(), self._lens[:n.value].copy()
+
     def state(self) -> dict:
         cap = self.num_pages
         bufs = [np.zeros(cap, np.int32) for _ in range(4)]
@@ -164,6 +175,31 @@ class KvCache:
         n = C.c_size_t()
         L.check(L.lib().kvc_attend_workspace_size(self._h, num_q, C.byref(n)), "kvc_attend_workspace_size")
         return n.value
+
+    def attend_subset(self, q, keep_ratio: float, seed: int, keep_first: int = 0, keep_last: int = 0, out=None,
+                      lse=None, sm_scale: Optional[float] = None, workspace=None, stream: Optional[int] = None):
+        """Attention of q [Lq, H, d] against a page subset of the visible table (kvc_attend_subset)."""
+        t = _torch()
+        dev = self.k_pool.device
+        if tuple(q.shape) != (q.shape[0], self.num_heads, self.head_dim) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [Lq, H, d] tensor")
+        if q.dtype != torch_dtype(self.dtype) or q.device != dev:
+            raise ValueError(f"q must be {self.dtype} on {dev}")
+        if out is None:
+            out = t.empty_like(q)
+        if lse is None:
+            lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
+        need = self.workspace_bytes(q.shape[0])
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = t.empty(need, dtype=t.uint8, device=dev)
+        wp = workspace.data_ptr() if need else None
+        wb = workspace.numel() * workspace.element_size() if need else 0
+        s = current_stream_ptr(dev) if stream is None else stream
+        scale = 0.0 if sm_scale is None else float(sm_scale)
+        L.check(L.lib().kvc_attend_subset(self._h, float(keep_ratio), int(seed) & (2**64 - 1), keep_first, keep_last,
+                                          q.data_ptr(), q.shape[0], scale, out.data_ptr(), lse.data_ptr(), wp, wb, s),
+                "kvc_attend_subset")
+        return out, lse
 
     def attend(self, q, out=None, lse=None, sm_scale: Optional[float] = None, num_splits: int = 0,
                workspace=None, stream: Optional[int] = None):

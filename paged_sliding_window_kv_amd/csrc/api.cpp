@@ -13,6 +13,7 @@
 #include "kernels.hpp"
 #include "kvc.h"
 #include "page_cache.hpp"
+#include "subset.hpp"
 
 struct kvc_cache {
   kvc::PageCache pc;
@@ -328,6 +329,37 @@ paged_attn_args cache_attn_args(const kvc_t* c, int32_t num_q, int32_t num_entri
   return a;
 }
 
+// kvc_attend with an explicit table (ids, lens; n <= kMaxInlinePages
+// entries of this cache's pool): the table travels in the launch arguments.
+int attend_inline(const kvc_t* c, const int32_t* ids, const int32_t* lens, int32_t n, const void* q, int32_t num_q,
+                  float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
+  if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache has no device pools");
+  if (num_q < 0 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "bad num_q or sm_scale");
+  if (num_q == 0) return KVC_OK;
+  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
+  if (c->pc.num_pages() > kvc::kInlineMaxPid + 1 || c->pc.config().page_size > 4095)
+    return fail(KVC_ERR_UNSUPPORTED, "pool too large for inline tables");
+  paged_attn_args a = cache_attn_args(c, num_q, n, sm_scale);
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (int s = check_attn_args(&a)) return s;
+  static thread_local kvc::AttnParamsInline pi;
+  int splits = 1;
+  if (int s = setup_attn(a, pi.base, &splits)) return s;
+  pi.num_entries = n;
+  pi.qo[0] = 0;
+  pi.qo[1] = num_q;
+  pi.kv[0] = 0;
+  pi.kv[1] = n;
+  for (int32_t i = 0; i < n; ++i)
+    pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
+  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,37 +389,50 @@ int kvc_attend_workspace_size(const kvc_t* c, int32_t num_q, size_t* bytes) {
 int kvc_attend(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
                void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
   if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache has no device pools");
-  if (num_q < 0 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
-    return fail(KVC_ERR_INVALID_ARGUMENT, "bad num_q or sm_scale");
-  if (num_q == 0) return KVC_OK;
-  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
   const int32_t n = c->pc.visible_count();
   if (n > kvc::kMaxInlinePages)
     return fail(KVC_ERR_UNSUPPORTED, "visible table has %d pages; kvc_attend passes at most %d (use paged_attn_fwd)",
                 n, kvc::kMaxInlinePages);
-  if (c->pc.num_pages() > kvc::kInlineMaxPid + 1 || c->pc.config().page_size > 4095)
-    return fail(KVC_ERR_UNSUPPORTED, "pool too large for inline tables");
-  paged_attn_args a = cache_attn_args(c, num_q, n, sm_scale);
-  a.q = q;
-  a.o = o;
-  a.lse = lse;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
-  if (int s = check_attn_args(&a)) return s;
-  static thread_local kvc::AttnParamsInline pi;
   int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
   c->pc.visible_table(ids, lens);
-  int splits = 1;
-  if (int s = setup_attn(a, pi.base, &splits)) return s;
-  pi.num_entries = n;
-  pi.qo[0] = 0;
-  pi.qo[1] = num_q;
-  pi.kv[0] = 0;
-  pi.kv[1] = n;
-  for (int32_t i = 0; i < n; ++i)
-    pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
-  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
+  return attend_inline(c, ids, lens, n, q, num_q, sm_scale, o, lse, workspace, workspace_bytes, stream);
+}
+
+int kvc_build_subset_table(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
+                           int32_t* page_ids, int32_t* page_lens, int32_t capacity, int32_t* num_pages) {
+  if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
+  if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
+  const int32_t n = c->pc.visible_count();
+  std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
+  c->pc.visible_table(ids.data(), lens.data());
+  std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
+  const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last, sid.data(),
+                                       slen.data());
+  *num_pages = m;
+  if (capacity < m || (m > 0 && (!page_ids || !page_lens)))
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "subset table needs %d entries", m);
+  std::copy(sid.begin(), sid.begin() + m, page_ids);
+  std::copy(slen.begin(), slen.begin() + m, page_lens);
+  return KVC_OK;
+}
+
+int kvc_attend_subset(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
+                      const void* q, int32_t num_q, float sm_scale, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, kvc_stream_t stream) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
+  if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
+  const int32_t n = c->pc.visible_count();
+  std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
+  c->pc.visible_table(ids.data(), lens.data());
+  std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
+  const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last,
+                                       sid.data(), slen.data());
+  if (m > kvc::kMaxInlinePages)
+    return fail(KVC_ERR_UNSUPPORTED, "subset table has %d pages; at most %d travel inline (use paged_attn_fwd)", m,
+                kvc::kMaxInlinePages);
+  return attend_inline(c, sid.data(), slen.data(), m, q, num_q, sm_scale, o, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
