@@ -10,6 +10,8 @@ Contents
               sliding window, special), the visible page table and the
               single-level rollback, exactly as written in the readings of
               the pages listed in the module docstring.
+  windowed    windowed inference: restart every window of kept units, the
+              last units of a window shared with the next.
   subset      page-subset visible tables (per-layer random page sampling)
               with the splitmix64 generator written out.
   attention   softmax attention in float64 over gathered pages, a dense
@@ -31,3 +33,4 @@ from .attention import (  # noqa: F401
     dense_history_attention,
 )
 from .subset import splitmix64, subset_table, subset_keep_count  # noqa: F401,E402
+from .windowed import OracleWindowed  # noqa: F401,E402

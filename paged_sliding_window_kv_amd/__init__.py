@@ -9,3 +9,4 @@ the library; the first call does, and raises if it has not been built.
 from ._lib import KvcError, NoUndo, OutOfPages, lib  # noqa: F401
 from .cache import KvCache, attend_batch, attend_batch_workspace_bytes, shared_pool_caches  # noqa: F401
 from .attention import paged_attention, merge_partials  # noqa: F401
+from .windowed import WindowedStream  # noqa: F401

@@ -1,0 +1,55 @@
+"""Windowed inference on the device: 25,000 frames, attention checked against the oracle, memory flat."""
+import pytest
+
+import synth
+from gpu_helpers import check_attention, log, to_dev
+from oracle import OracleCache, OracleConfig, OracleWindowed, attention_f64, is_keyframe
+from oracle import to_f64 as bits_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_windowed_stream_25000_frames():
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, WindowedStream
+    H, P, X, S, W, N = 2, 256, 6, 8, 64, 2
+    slots, overlap, frames = 128, 16, 25000
+    log(f"windowed stream: {frames} frames, window {slots} slots, overlap {overlap}, keyframe interval {N}")
+    bank = [synth.frame_qkv(70, 0, i, P + X, H, 64, "bf16") for i in range(7)]
+    dev_bank = [tuple(to_dev(x, "bf16") for x in f) for f in bank]
+    oc = OracleWindowed(OracleCache(OracleConfig(num_heads=H, head_dim=64, patch_tokens=P, special_tokens=X,
+                                                 num_scale_units=S, window_units=W, max_units=slots + 1,
+                                                 store_dtype="bf16")), slots, overlap)
+    dc = KvCache(num_heads=H, dtype="bf16", patch_tokens=P, special_tokens=X, num_scale_units=S, window_units=W,
+                 max_units=slots + 1, device="cuda")
+    ws = WindowedStream(dc, slots, overlap)
+    o = torch.empty((P + X, H, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((P + X, H), dtype=torch.float32, device="cuda")
+    wsp = torch.empty(max(dc.workspace_bytes(P + X), 256), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    checks = 0
+    for t in range(frames):
+        b = (t * 3) % len(bank)
+        q, k, v = bank[b]
+        dq, dk, dv = dev_bank[b]
+        r1 = oc.append(k, v)
+        r2 = ws.append(dk, dv)
+        assert r1 == r2
+        if t % 3125 == 0 or t == frames - 1 or (r2 and ws.windows in (1, 2)):
+            dc.attend(dq, o, lse, workspace=wsp)
+            gk, gv = oc.cache.gather()
+            ro, rl = attention_f64(bits_f64(q), bits_f64(gk), bits_f64(gv))
+            check_attention(o, lse, ro, rl, "bf16", f"t={t} window {ws.windows} Lk={gk.shape[1]}")
+            checks += 1
+        if is_keyframe(t, S, N):
+            oc.keep()
+            ws.keep()
+        else:
+            oc.drop()
+            ws.drop()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    assert ws.windows == oc.windows and ws.windows > 90
+    assert dc.state() == oc.cache.state()
+    assert checks >= 10
