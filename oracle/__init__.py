@@ -12,6 +12,8 @@ Contents
               the pages listed in the module docstring.
   windowed    windowed inference: restart every window of kept units, the
               last units of a window shared with the next.
+  fp8         FP8 (E4M3) KV pages: per-(token, head) power-of-two row
+              scales, round-to-nearest-even quantisation and dequantisation.
   subset      page-subset visible tables (per-layer random page sampling)
               with the splitmix64 generator written out.
   attention   softmax attention in float64 over gathered pages, a dense
@@ -34,3 +36,4 @@ from .attention import (  # noqa: F401
 )
 from .subset import splitmix64, subset_table, subset_keep_count  # noqa: F401,E402
 from .windowed import OracleWindowed  # noqa: F401,E402
+from .fp8 import E4M3_MAX, dequantize_rows, e4m3_decode, e4m3_encode, quantize_rows, row_exponent  # noqa: F401,E402

@@ -45,6 +45,9 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
+from .attention import bf16_bits_to_f64
+from .fp8 import dequantize_rows, quantize_rows
+
 FRAME_ALIGNED = 0
 CONTIGUOUS = 1
 
@@ -69,7 +72,7 @@ class OracleConfig:
     special_packing: int = FRAME_ALIGNED
     max_units: int = 1000
     num_pages: int = 0              # 0: derive with required_pages
-    store_dtype: str = "bf16"       # "bf16" -> uint16 patterns, "f32" -> float32
+    store_dtype: str = "bf16"       # "bf16" -> uint16 patterns, "f32" -> float32, "fp8" -> E4M3 codes + exponents
 
     @property
     def unit_pages(self) -> int:
@@ -131,11 +134,15 @@ class OracleCache:
         self.cfg = cfg
         self.num_pages = cfg.num_pages or required_pages(cfg)
         self.with_pool = with_pool
-        dt = np.uint16 if cfg.store_dtype == "bf16" else np.float32
+        dt = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[cfg.store_dtype]
         if with_pool:
             shape = (self.num_pages, cfg.num_heads, cfg.page_size, cfg.head_dim)
             self.k_pool = np.zeros(shape, dt)
             self.v_pool = np.zeros(shape, dt)
+            if cfg.store_dtype == "fp8":
+                # per-(token, head) row exponents of the FP8 pages (oracle/fp8.py)
+                self.k_exp = np.zeros(shape[:3], np.int8)
+                self.v_exp = np.zeros(shape[:3], np.int8)
         self.reset()
 
     # -- state ---------------------------------------------------------------
@@ -213,14 +220,25 @@ class OracleCache:
         prev_fill = self.fill
         self.special_pages.extend(opened)
         if self.with_pool:
+            fp8 = cfg.store_dtype == "fp8"
+            if fp8:
+                # bf16 input rows quantised per (token, head) as they are appended
+                kc, ke = quantize_rows(bf16_bits_to_f64(k_unit))
+                vc, ve = quantize_rows(bf16_bits_to_f64(v_unit))
+            else:
+                kc, vc = k_unit, v_unit
+
+            def put(pg, slot, i):
+                self.k_pool[pg, :, slot, :] = kc[i]
+                self.v_pool[pg, :, slot, :] = vc[i]
+                if fp8:
+                    self.k_exp[pg, :, slot] = ke[i]
+                    self.v_exp[pg, :, slot] = ve[i]
+
             for i in range(cfg.patch_tokens):
-                pg, slot = unit[i // cfg.page_size], i % cfg.page_size
-                self.k_pool[pg, :, slot, :] = k_unit[i]
-                self.v_pool[pg, :, slot, :] = v_unit[i]
+                put(unit[i // cfg.page_size], i % cfg.page_size, i)
             for j, (pidx, slot) in enumerate(sslots):
-                pg = self.special_pages[pidx]
-                self.k_pool[pg, :, slot, :] = k_unit[cfg.patch_tokens + j]
-                self.v_pool[pg, :, slot, :] = v_unit[cfg.patch_tokens + j]
+                put(self.special_pages[pidx], slot, cfg.patch_tokens + j)
         if cfg.special_tokens:
             if cfg.special_packing == FRAME_ALIGNED:
                 self.fill = 1 if new_special else self.fill + 1
@@ -297,10 +315,19 @@ class OracleCache:
 
     # -- gather --------------------------------------------------------------
     def gather(self, ids: Optional[List[int]] = None, lens: Optional[List[int]] = None):
-        """Visible K and V as [H, Lk, d] arrays in the store dtype, in table order."""
+        """Visible K and V as [H, Lk, d] arrays in the store dtype, in table order.
+
+        FP8 caches return the dequantised values (float64, code * 2^e)."""
         if ids is None:
             ids, lens = self.visible_table()
         cfg = self.cfg
+        if cfg.store_dtype == "fp8":
+            if not ids:
+                e = np.zeros((cfg.num_heads, 0, cfg.head_dim))
+                return e, e.copy()
+            ks = [dequantize_rows(self.k_pool[p, :, :n, :], self.k_exp[p, :, :n]) for p, n in zip(ids, lens)]
+            vs = [dequantize_rows(self.v_pool[p, :, :n, :], self.v_exp[p, :, :n]) for p, n in zip(ids, lens)]
+            return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
         dt = self.k_pool.dtype
         if not ids:
             e = np.zeros((cfg.num_heads, 0, cfg.head_dim), dt)
