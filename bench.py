@@ -54,9 +54,19 @@ def attn_flops(lq: int, lk: int, heads: int, d: int = 64) -> float:
     return 4.0 * lq * lk * d * heads
 
 
-def attn_bytes(lq: int, lk: int, heads: int, d: int = 64, elem: int = 2) -> float:
-    """Bytes an attention call must move: K and V of the visible tokens, Q in, O out, LSE out."""
-    return 2.0 * lk * heads * d * elem + 2.0 * lq * heads * d * elem + lq * heads * 4.0
+def attn_bytes(lq: int, lk: int, heads: int, d: int = 64, elem: int = 2, kv_elem: float = 2.0) -> float:
+    """Bytes an attention call must move: K and V of the visible tokens, Q in, O out, LSE out.
+
+    kv_elem: bytes per K/V value (2 for bf16 pages, 1 + 1/d for FP8 codes with a row exponent)."""
+    return 2.0 * lk * heads * d * kv_elem + 2.0 * lq * heads * d * elem + lq * heads * 4.0
+
+
+def kv_label(kv_dtype: str) -> str:
+    return "bf16" if kv_dtype == "bf16" else "bf16 activations, FP8 (E4M3) KV pages with per-token exponents"
+
+
+def kv_elem_bytes(kv_dtype: str, d: int = 64) -> float:
+    return 2.0 if kv_dtype == "bf16" else 1.0 + 1.0 / d
 
 
 def blas_threads() -> int:
@@ -84,7 +94,7 @@ def stream_lk(t: int, c=STREAM) -> int:
 
 
 class StreamBench:
-    def __init__(self, frames: int, layers: int, bank: int = 4, seed: int = 0):
+    def __init__(self, frames: int, layers: int, bank: int = 4, seed: int = 0, kv_dtype: str = "bf16"):
         import torch
         from paged_sliding_window_kv_amd import KvCache, lib
         c = STREAM
@@ -96,7 +106,8 @@ class StreamBench:
         self.lib = lib()
         dev = torch.device("cuda:0")
         self.dev = dev
-        self.caches = [KvCache(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], dtype="bf16",
+        self.kv_elem = kv_elem_bytes(kv_dtype, c["d"])
+        self.caches = [KvCache(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], dtype=kv_dtype,
                                patch_tokens=c["patch"], special_tokens=c["special"], num_scale_units=c["scale"],
                                window_units=c["window"], max_units=max(frames, 64), device=dev)
                        for _ in range(layers)]
@@ -197,7 +208,7 @@ class StreamBench:
             ev1.synchronize()
             tot += ev0.elapsed_time(ev1) * 1e-3
             lk = stream_lk(t, c)
-            byt += self.layers * attn_bytes(self.tokens, lk, c["heads"], c["d"])
+            byt += self.layers * attn_bytes(self.tokens, lk, c["heads"], c["d"], kv_elem=self.kv_elem)
             flo += self.layers * attn_flops(self.tokens, lk, c["heads"], c["d"])
         return tot, byt, flo
 
@@ -239,7 +250,7 @@ def run_stream(args) -> dict:
     import torch
     frames, layers = args.steps, STREAM["layers"]
     log(f"[bench] stream: {layers} layers x {frames} frames, warmup {args.warmup}")
-    b = StreamBench(max(frames, args.warmup), layers)
+    b = StreamBench(max(frames, args.warmup), layers, kv_dtype=args.kv_dtype)
     if args.warmup:
         b.run(args.warmup)
         torch.cuda.synchronize()
@@ -262,11 +273,13 @@ def run_stream(args) -> dict:
         "frames_per_s": fps,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "config": {
-            "workload": "lingbot_stream: 24 layer caches, 16 heads x 64, bf16, 256 patch + 6 special tokens/frame, "
+            "workload": f"lingbot_stream: 24 layer caches, 16 heads x 64, {kv_label(args.kv_dtype)}, "
+                        "256 patch + 6 special tokens/frame, "
                         "8 scale frames, 64-frame window, 42 frames/special page, 262 queries/step, "
                         f"{frames} frames",
             "layers": layers, "heads": 16, "head_dim": 64, "page_size": 256, "frames": frames,
-            "final_visible_tokens": lk_sum, "final_visible_pages": npages,
+            "final_visible_tokens": lk_sum, "final_visible_pages": npages, "kv_dtype": args.kv_dtype,
+            "kv_pool_mib_per_layer": (b.caches[0].k_pool.numel() * b.caches[0].k_pool.element_size() * 2) / 2**20,
         },
         "roofline": {
             "bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -615,6 +628,8 @@ def main():
     ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global", "stream_batched"])
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="stream: KV page type (fp8 = E4M3 codes with per-token exponents, RFC section 3.4)")
     ap.add_argument("--keep-ratio", type=float, default=1.0,
                     help="chunked: attend to a per-layer random page subset keeping this fraction (AVGGT-style)")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
@@ -636,7 +651,7 @@ def main():
         args.steps = {"stream": 1000, "chunked": 8, "global": 1, "stream_batched": 1000}[args.workload]
     if args.workload == "stream":
         res = run_stream(args)
-        ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md")
+        ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md") if args.kv_dtype == "bf16" else None
         if ratio is not None:
             res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
             res["roofline"]["traffic_ratio"] = ratio

@@ -45,6 +45,15 @@
  *   Element type is bf16 (2 bytes) or fp32 (4 bytes), per kvc_config.dtype.
  *   K/V/Q/O activations are [tokens][H][d], tokens in order.
  *
+ *   FP8 caches (KVC_DTYPE_FP8_E4M3; "vLLM-Omni RFC #2727", section 3.4,
+ *   item 5: KV cache FP8 for about half the memory) store K and V both
+ *   slot-major, [num_pages][H][P][d] bytes of OCP E4M3 codes, followed in the
+ *   same buffer by [num_pages][H][P] int8 row exponents e.  Row (page, head,
+ *   slot) holds the token's d values as code * 2^e, e being the smallest
+ *   integer in [-127, 127] with max|x| <= 448 * 2^e, each value rounded to
+ *   the nearest E4M3 value (ties to even).  Appends take bf16 K/V and quantise
+ *   them; attention takes bf16 q and writes bf16 o.
+ *
  * Streams and threads
  *   Device work is enqueued on the hipStream_t passed in (0 = null stream)
  *   and is asynchronous to the host.  A handle is not thread-safe; use one
@@ -78,7 +87,7 @@ typedef enum kvc_status {
   KVC_ERR_DEVICE = -6,
 } kvc_status;
 
-typedef enum kvc_dtype { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F32 = 1 } kvc_dtype;
+typedef enum kvc_dtype { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F32 = 1, KVC_DTYPE_FP8_E4M3 = 2 } kvc_dtype;
 
 typedef enum kvc_special_packing {
   /* floor(P / special_tokens) whole frames per special page (42 for 6 tokens
@@ -131,7 +140,8 @@ typedef struct kvc_cache kvc_t;
  * special pages of max_units units; with an unbounded window, max_units units. */
 int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages);
 
-/* Bytes of one pool (K or V): num_pages * H * P * d * sizeof(element). */
+/* Bytes of one pool (K or V): num_pages * H * P * d * sizeof(element); for
+ * FP8 caches num_pages * H * P * (d + 1) (codes and row exponents). */
 int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes);
 
 /* Create a cache.  k_pool / v_pool: caller-owned device buffers of
@@ -144,7 +154,8 @@ int kvc_destroy(kvc_t* cache);
 /* Append one unit ("LingBot-Map Paged KV Cache", section 2; RFC #2727,
  * section 3.3: KV append, then eviction of the oldest chunk beyond the
  * window).  k_unit / v_unit: device [patch_tokens + special_tokens][H][d],
- * patch tokens first, in the cache dtype; both NULL on a host-only handle.
+ * patch tokens first, in the cache dtype (bf16 for FP8 caches, quantised by
+ * the append); both NULL on a host-only handle.
  * Plans on the host and enqueues one scatter kernel on `stream`.
  * KVC_ERR_OUT_OF_PAGES when the free list cannot supply the unit. */
 int kvc_append_frame(kvc_t* cache, const void* k_unit, const void* v_unit, kvc_stream_t stream);
@@ -177,7 +188,7 @@ int kvc_get_state(const kvc_t* cache, kvc_state* out);
 /* ------------------------------------------------------------------------ */
 
 typedef struct paged_attn_args {
-  int32_t dtype;            /* kvc_dtype of q, pools and o */
+  int32_t dtype;            /* kvc_dtype of q, pools and o (FP8 pools: q and o bf16) */
   int32_t num_heads;        /* H */
   int32_t head_dim;         /* d = 64 */
   int32_t page_size;        /* P, multiple of 64 */

@@ -22,6 +22,7 @@ KVC_ERR_DEVICE = -6
 
 KVC_DTYPE_BF16 = 0
 KVC_DTYPE_F32 = 1
+KVC_DTYPE_FP8_E4M3 = 2
 KVC_SPECIAL_FRAME_ALIGNED = 0
 KVC_SPECIAL_CONTIGUOUS = 1
 

@@ -14,7 +14,7 @@ import numpy as np
 
 from . import _lib as L
 
-_DTYPES = {"bf16": L.KVC_DTYPE_BF16, "f32": L.KVC_DTYPE_F32}
+_DTYPES = {"bf16": L.KVC_DTYPE_BF16, "f32": L.KVC_DTYPE_F32, "fp8": L.KVC_DTYPE_FP8_E4M3}
 _PACKING = {"frame_aligned": L.KVC_SPECIAL_FRAME_ALIGNED, "contiguous": L.KVC_SPECIAL_CONTIGUOUS}
 
 
@@ -24,8 +24,9 @@ def _torch():
 
 
 def torch_dtype(dtype: str):
+    """Activation dtype (K/V appended, q, o) of a cache dtype; FP8 caches take and give bf16."""
     t = _torch()
-    return {"bf16": t.bfloat16, "f32": t.float32}[dtype]
+    return {"bf16": t.bfloat16, "f32": t.float32, "fp8": t.bfloat16}[dtype]
 
 
 def current_stream_ptr(device=None) -> int:
@@ -40,6 +41,10 @@ class KvCache:
     page metadata moves (useful to check tables without a GPU).  Otherwise the
     K pool [num_pages, H, P, d] and the V pool [num_pages, H, d, P] are
     allocated on `device` and appends scatter device K/V into them.
+    dtype "fp8": the pools are flat uint8 buffers of OCP E4M3 codes, both
+    slot-major [num_pages, H, P, d], followed by int8 row exponents
+    [num_pages, H, P] (views: k_codes, k_exps, v_codes, v_exps); appends
+    take bf16 K/V and quantise them, attention takes bf16 q.
     """
 
     def __init__(self, num_heads: int, head_dim: int = 64, page_size: int = 256, dtype: str = "bf16",
@@ -59,7 +64,16 @@ class KvCache:
         self.num_pages = n.value
         self.device = device
         self.k_pool = self.v_pool = None
-        if pools is not None:
+        if dtype == "fp8":
+            if pools is not None:
+                raise ValueError("FP8 caches allocate their own pools")
+            if device is not None:
+                t = _torch()
+                nb = C.c_size_t()
+                L.check(lib.kvc_pool_bytes(C.byref(self.cfg), C.byref(nb)), "kvc_pool_bytes")
+                self.k_pool = t.empty(nb.value, dtype=t.uint8, device=device)
+                self.v_pool = t.empty(nb.value, dtype=t.uint8, device=device)
+        elif pools is not None:
             # caller-owned pool tensors (e.g. page slices of a pool shared by a batch)
             k_pool, v_pool = pools
             want_k = (self.num_pages, num_heads, page_size, head_dim)
@@ -80,6 +94,14 @@ class KvCache:
         h = C.c_void_p()
         L.check(lib.kvc_create(C.byref(self.cfg), self._ptr(self.k_pool), self._ptr(self.v_pool), C.byref(h)),
                 "kvc_create")
+        if dtype == "fp8" and self.k_pool is not None:
+            ncode = self.num_pages * num_heads * page_size * head_dim
+            shp = (self.num_pages, num_heads, page_size, head_dim)
+            t = _torch()
+            self.k_codes = self.k_pool[:ncode].view(shp)
+            self.v_codes = self.v_pool[:ncode].view(shp)
+            self.k_exps = self.k_pool[ncode:].view(t.int8).view(shp[:3])
+            self.v_exps = self.v_pool[ncode:].view(t.int8).view(shp[:3])
         self._h = h
         self._ids = np.zeros(self.num_pages, np.int32)
         self._lens = np.zeros(self.num_pages, np.int32)
@@ -239,9 +261,10 @@ class KvCache:
         page_lens = t.from_numpy(lens).to(dev)
         qo = t.tensor([0, q.shape[0]], dtype=t.int32, device=dev)
         kv = t.tensor([0, len(ids)], dtype=t.int32, device=dev)
+        fp8 = (self.num_pages, self.page_size) if self.dtype == "fp8" else None
         return paged_attention(q, self.k_pool, self.v_pool, page_ids, page_lens, qo, kv,
                                max_qo_len=q.shape[0], max_kv_pages=len(ids), out=out, lse=lse,
-                               sm_scale=sm_scale, num_splits=num_splits, stream=stream)
+                               sm_scale=sm_scale, num_splits=num_splits, stream=stream, fp8_pages=fp8)
 
 
 def shared_pool_caches(count: int, device, **cfg) -> list:

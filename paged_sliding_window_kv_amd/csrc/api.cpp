@@ -37,7 +37,13 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-size_t elem_size(int dtype) { return dtype == KVC_DTYPE_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == KVC_DTYPE_BF16 ? 2 : dtype == KVC_DTYPE_F32 ? 4 : 1; }
+
+// Bytes of one pool: elements, plus the row exponents of FP8 pools.
+size_t pool_bytes(const kvc_config& c, int32_t pages) {
+  const size_t rows = static_cast<size_t>(pages) * c.num_heads * c.page_size;
+  return rows * c.head_dim * elem_size(c.dtype) + (c.dtype == KVC_DTYPE_FP8_E4M3 ? rows : 0);
+}
 
 bool device_shapes_ok(const kvc_config& c) {
   return c.head_dim == kvc::kHeadDim && c.page_size % kvc::kKeyTile == 0;
@@ -54,7 +60,7 @@ int choose_waves(const paged_attn_args& a) {
 }
 
 int rows_per_tile(const paged_attn_args& a) {
-  return a.dtype == KVC_DTYPE_BF16 ? kvc::attn_bf16_rows_per_tile(choose_waves(a)) : kvc::attn_f32_rows_per_tile();
+  return a.dtype != KVC_DTYPE_F32 ? kvc::attn_bf16_rows_per_tile(choose_waves(a)) : kvc::attn_f32_rows_per_tile();
 }
 
 int choose_splits(const paged_attn_args& a) {
@@ -65,7 +71,7 @@ int choose_splits(const paged_attn_args& a) {
   // Aim for about one round of workgroups over the 256 compute units (two per
   // unit for narrow workgroups), keeping at least two pages per split so the
   // merge traffic stays small against the K/V reads.
-  const int waves = a.dtype == KVC_DTYPE_BF16 ? choose_waves(a) : 1;
+  const int waves = a.dtype != KVC_DTYPE_F32 ? choose_waves(a) : 1;
   const long target = waves <= 4 ? 512 : 256;
   if (tiles >= target) return 1;
   long s = (target + tiles - 1) / tiles;
@@ -75,7 +81,7 @@ int choose_splits(const paged_attn_args& a) {
 
 int check_attn_args(const paged_attn_args* a) {
   if (!a) return fail(KVC_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->dtype != KVC_DTYPE_BF16 && a->dtype != KVC_DTYPE_F32)
+  if (a->dtype != KVC_DTYPE_BF16 && a->dtype != KVC_DTYPE_F32 && a->dtype != KVC_DTYPE_FP8_E4M3)
     return fail(KVC_ERR_INVALID_ARGUMENT, "bad dtype %d", a->dtype);
   if (a->head_dim != kvc::kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "head_dim %d (kernels need 64)", a->head_dim);
   if (a->page_size <= 0 || a->page_size % kvc::kKeyTile != 0)
@@ -131,7 +137,7 @@ int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes) {
   if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
   const int32_t n = cfg->num_pages > 0 ? cfg->num_pages : kvc::PageCache::required_pages(*cfg);
   if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
-  *bytes = static_cast<size_t>(n) * cfg->num_heads * cfg->page_size * cfg->head_dim * elem_size(cfg->dtype);
+  *bytes = pool_bytes(*cfg, n);
   return KVC_OK;
 }
 
@@ -185,6 +191,12 @@ int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_strea
   p.special_count0 = plan.special_count0;
   p.special_page1 = plan.special_page1;
   p.num_unit_pages = static_cast<int32_t>(plan.unit_pages.size());
+  if (cfg.dtype == KVC_DTYPE_FP8_E4M3) {
+    // row exponents follow the codes in each pool buffer
+    const size_t codes = static_cast<size_t>(c->pc.num_pages()) * cfg.num_heads * cfg.page_size * cfg.head_dim;
+    p.k_exp = static_cast<char*>(c->k_pool) + codes;
+    p.v_exp = static_cast<char*>(c->v_pool) + codes;
+  }
   std::copy(plan.unit_pages.begin(), plan.unit_pages.end(), p.unit_pages);
   const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -299,11 +311,14 @@ int setup_attn(const paged_attn_args& a, kvc::AttnParams& p, int* splits_out) {
 template <class Src>
 int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_t st) {
   const kvc::AttnParams& p = kvc::attn_base(src);
-  hipError_t e = a.dtype == KVC_DTYPE_BF16 ? kvc::launch_attn_bf16(src, choose_waves(a), st)
-                                           : kvc::launch_attn_f32(src, st);
+  hipError_t e = a.dtype == KVC_DTYPE_BF16        ? kvc::launch_attn_bf16(src, choose_waves(a), st)
+                 : a.dtype == KVC_DTYPE_FP8_E4M3 ? kvc::launch_attn_fp8kv(src, choose_waves(a), st)
+                                                 : kvc::launch_attn_f32(src, st);
   if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
   if (splits > 1) {
-    e = kvc::launch_attn_merge(a.dtype, splits, a.total_q, a.num_heads, p.part_o, p.part_lse, a.o, a.lse, st);
+    // o is bf16 for FP8 caches
+    const int odt = a.dtype == KVC_DTYPE_F32 ? KVC_DTYPE_F32 : KVC_DTYPE_BF16;
+    e = kvc::launch_attn_merge(odt, splits, a.total_q, a.num_heads, p.part_o, p.part_lse, a.o, a.lse, st);
     if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   }
   return KVC_OK;
@@ -459,6 +474,9 @@ int batch_args(const kvc_t* const* caches, int32_t n, const int32_t* qo, float s
     if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL cache in batch");
     if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache %d has no device pools", i);
     const kvc_config& g = c->pc.config();
+    if (g.dtype == KVC_DTYPE_FP8_E4M3)
+      return fail(KVC_ERR_UNSUPPORTED, "cache %d: FP8 caches are not batched (their exponents sit at the end of "
+                  "each cache's own pool buffer)", i);
     if (g.num_heads != f.num_heads || g.head_dim != f.head_dim || g.page_size != f.page_size || g.dtype != f.dtype)
       return fail(KVC_ERR_INVALID_ARGUMENT, "cache %d: heads, head_dim, page_size and dtype must match the batch", i);
     if (qo[i + 1] < qo[i]) return fail(KVC_ERR_INVALID_ARGUMENT, "qo_indptr must be non-decreasing");

@@ -179,13 +179,23 @@ __device__ __forceinline__ void cursor_next(const Src& src, int ee, Cursor& c) {
   }
 }
 
-template <int NB, bool XB, class Src>
+// KV8: the pools hold FP8 (OCP E4M3) codes with per-(token, head) int8 row
+// exponents (layout in kvc.h).  The ring then stages the codes and exponents
+// of each tile (8,320 bytes), and after each pair's barrier the workgroup
+// converts the pair into the bf16 tile layout of `lds` (two tiles), with
+// v_cvt_scalef32_pk_bf16_fp8 applying 2^e; every later step is the bf16
+// kernel's.  The dequantised values are exactly bf16 numbers (3-bit
+// mantissas times powers of two).
+template <int NB, bool XB, class Src, bool KV8 = false>
 __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   static_assert(!XB || NB >= 4, "the extra block is shared by waves 0..3");
   const AttnParams& p = attn_base(src);
   constexpr int ROWS = (NB + (XB ? 1 : 0)) * 32;
   constexpr int LPT = (DMA_PER_TILE + NB - 1) / NB;  // direct loads per wave per tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[STAGES][2][TILE_ELEMS];
+  constexpr int NBUF = KV8 ? 2 : STAGES;            // bf16 tiles: the ring, or the converted pair
+  constexpr int STAGE8 = 2 * TILE_ELEMS + 2 * KT;   // FP8 stage: K codes, V codes, K exps, V exps
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds8[KV8 ? STAGES : 1][KV8 ? STAGE8 : 16];
   __shared__ __attribute__((aligned(16))) uint16_t lds_q[ROWS * D];  // this tile's queries, swizzled rows
 
   // ---- which (sequence, head, split, query tile) ----------------------------
@@ -264,13 +274,79 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
     dma_goff[j] = is_v ? row * P + chunk * 8 : row * D + chunk * 8;
     dma_loff[j] = is_v * TILE_ELEMS + part * 512;
   }
-  auto issue = [&](const Cursor& c, int stage) {
-    const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
-    const int koff = c.kt * KT * D, voff = c.kt * KT;
+  // KV8 loads: inst 0-3 K codes (1 KiB each), 4-7 V codes, 8-11 K exponents
+  // and 12-15 V exponents (16 bytes each, lane 0 only).  Stage bytes:
+  // [0, 4096) K codes [slot][dim], [4096, 8192) V codes [slot][dim],
+  // [8192, 8256) K exponents, [8256, 8320) V exponents.
+  int dma8_kind[LPT], dma8_off[LPT];
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
-      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds[stage][0][0] + dma_loff[j]), 16, 0, 0);
+  for (int j = 0; j < LPT; ++j) {
+    const int inst = min(wave * LPT + j, DMA_PER_TILE - 1);
+    const int kind = inst >> 2, q = inst & 3;
+    dma8_kind[j] = kind;
+    dma8_off[j] = kind < 2 ? kind * 4096 + q * 1024 : 8192 + (kind - 2) * KT + q * 16;
+  }
+  const uint8_t* __restrict__ kg8 = static_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* __restrict__ vg8 = static_cast<const uint8_t*>(p.v_pool);
+  const size_t codes_bytes = static_cast<size_t>(p.num_pool_pages) * H * P * D;  // exponents follow
+  auto issue = [&](const Cursor& c, int stage) {
+    if constexpr (KV8) {
+      const size_t row0 = (static_cast<size_t>(c.pid) * H + h) * P + c.kt * KT;  // first slot row of the tile
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int kind = dma8_kind[j];
+        const uint8_t* base = (kind & 1) ? vg8 : kg8;
+        if (kind < 2) {
+          // (the source goes in as const void*: a byte pointer there leaves the
+          // host side of this instantiation without its launch stub)
+          const void* gp = base + row0 * D + (dma8_off[j] & 4095) + lane * 16;
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds8[stage][0] + dma8_off[j]), 16, 0, 0);
+        } else if (lane == 0) {
+          const void* gp = base + codes_bytes + row0 + (dma8_off[j] - 8192 - (kind - 2) * KT);
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds8[stage][0] + dma8_off[j]), 16, 0, 0);
+        }
+      }
+    } else {
+      const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
+      const int koff = c.kt * KT * D, voff = c.kt * KT;
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
+        __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds[stage][0][0] + dma_loff[j]), 16, 0, 0);
+      }
+    }
+  };
+  // KV8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`:
+  // K rows keep their layout; V rows become V^T rows (dims) in the pool slot
+  // order v_slot_pos with the chunk swizzle.  Keys past nk become zeros.
+  auto convert = [&](int stage, int b, int nk) {
+    const uint8_t* st8 = &lds8[stage][0];
+    for (int it = tid; it < 2 * KT * 8; it += NB * 64) {
+      const bool is_v = it >= KT * 8;
+      const int r = (it >> 3) & (KT - 1), ch = it & 7;  // token, 8-dim chunk
+      const uint2 w = *reinterpret_cast<const uint2*>(st8 + (is_v ? 4096 : 0) + r * D + ch * 8);
+      const int e = static_cast<int8_t>(st8[8192 + (is_v ? KT : 0) + r]);
+      const float sc = __builtin_ldexpf(1.f, e);
+      typedef __bf16 bf16x2_ __attribute__((__vector_size__(2 * sizeof(__bf16))));
+      bf16x2_ v2[4];
+      v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, false);
+      v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, true);
+      v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, false);
+      v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, true);
+      uint32_t u[4];
+      __builtin_memcpy(u, v2, sizeof u);
+      if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
+      if (!is_v) {
+        *reinterpret_cast<uint4*>(&lds[b][0][0] + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
+      } else {
+        const int pos = v_slot_pos(r);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = ch * 8 + j;  // dim
+          lds[b][1][row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
+              static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1)));
+        }
+      }
     }
   };
   // Zero the V^T slots of keys nk..63 of a staged tile.  In a pool row, key k
@@ -329,11 +405,17 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
       nkb = min(KT, cb.len - cb.kt * KT);
     }
     const int sa = nc % STAGES, sb = (nc + 1) % STAGES;
-    const uint16_t* lka = lds[sa][0];
-    uint16_t* lva = lds[sa][1];
-    const uint16_t* lkb = lds[sb][0];
-    uint16_t* lvb = lds[sb][1];
-    if (nka < KT || (two && nkb < KT)) {
+    const uint16_t* lka = lds[KV8 ? 0 : sa][0];
+    uint16_t* lva = lds[KV8 ? 0 : sa][1];
+    const uint16_t* lkb = lds[KV8 ? 1 : sb][0];
+    uint16_t* lvb = lds[KV8 ? 1 : sb][1];
+    if constexpr (KV8) {
+      // Everyone is done with the previous pair's bf16 tiles (barrier above).
+      convert(sa, 0, nka);
+      if (two) convert(sb, 1, nkb);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+      __builtin_amdgcn_s_barrier();
+    } else if (nka < KT || (two && nkb < KT)) {
       if (nka < KT) zero_tail(lva, nka);
       if (two && nkb < KT) zero_tail(lvb, nkb);
       __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
@@ -622,14 +704,14 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
 // waves <= 8: that many 32-row blocks; 9: eight waves plus the shared extra block.
 int attn_bf16_rows_per_tile(int waves) { return waves * 32; }
 
-template <class Src>
+template <bool KV8, class Src>
 static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
   const AttnParams& p = attn_base(src);
   const dim3 grid(static_cast<unsigned>(p.q_tiles) * p.groups_padded);
   switch (waves) {
-#define KVC_CASE(W)                                                                               \
-  case W:                                                                                         \
-    hipLaunchKernelGGL((attn_bf16_kernel<W, false, Src>), grid, dim3(W * 64), 0, stream, src); \
+#define KVC_CASE(W)                                                                                    \
+  case W:                                                                                              \
+    hipLaunchKernelGGL((attn_bf16_kernel<W, false, Src, KV8>), grid, dim3(W * 64), 0, stream, src); \
     break;
     KVC_CASE(1)
     KVC_CASE(2)
@@ -641,7 +723,7 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
     KVC_CASE(8)
 #undef KVC_CASE
     case 9:
-      hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src>), grid, dim3(8 * 64), 0, stream, src);
+      hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 64), 0, stream, src);
       break;
     default:
       return hipErrorInvalidValue;
@@ -650,10 +732,16 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream) {
-  return launch_impl(p, waves, stream);
+  return launch_impl<false>(p, waves, stream);
 }
 hipError_t launch_attn_bf16(const AttnParamsInline& p, int waves, hipStream_t stream) {
-  return launch_impl(p, waves, stream);
+  return launch_impl<false>(p, waves, stream);
+}
+hipError_t launch_attn_fp8kv(const AttnParams& p, int waves, hipStream_t stream) {
+  return launch_impl<true>(p, waves, stream);
+}
+hipError_t launch_attn_fp8kv(const AttnParamsInline& p, int waves, hipStream_t stream) {
+  return launch_impl<true>(p, waves, stream);
 }
 
 }  // namespace kvc

@@ -36,6 +36,8 @@ struct AppendParams {
   int32_t special_count0;
   int32_t special_page1;
   int32_t num_unit_pages;
+  void* k_exp;            // FP8 caches: row exponents [pages][H][P] (int8), after the codes
+  void* v_exp;
   int32_t unit_pages[kMaxUnitPages];
 };
 
@@ -129,6 +131,9 @@ __device__ __forceinline__ void attn_entry(const AttnParamsInline& p, int e, int
 int attn_bf16_rows_per_tile(int waves);
 hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParamsInline& p, int waves, hipStream_t stream);
+// FP8 (E4M3) pools with row exponents; q and o bf16.  Same row tiling as the bf16 kernel.
+hipError_t launch_attn_fp8kv(const AttnParams& p, int waves, hipStream_t stream);
+hipError_t launch_attn_fp8kv(const AttnParamsInline& p, int waves, hipStream_t stream);
 int attn_f32_rows_per_tile();
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParamsInline& p, hipStream_t stream);

@@ -108,6 +108,95 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const AppendParams 
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 caches ("vLLM-Omni RFC #2727", section 3.4, item 5: KV cache FP8).
+// Each (token, head) row of d = 64 bf16 values becomes 64 OCP E4M3 codes and
+// one int8 exponent e: e is the smallest integer in [-127, 127] with
+// max|x| <= 448 * 2^e, and each code is x / 2^e rounded to the nearest E4M3
+// value, ties to the even code.  K and V rows both go slot-major into
+// their pools; the exponents go to [page][head][slot] after the codes.
+// ---------------------------------------------------------------------------
+
+// Smallest e in [-127, 127] with amax <= 448 * 2^e (-127 for amax = 0).
+__device__ __forceinline__ int fp8_row_exponent(float amax) {
+  if (amax == 0.f) return -127;
+  int fe;
+  const float fm = frexpf(amax, &fe);  // amax = fm * 2^fe, fm in [0.5, 1)
+  const int E = fe - 1;
+  const int e = (2.f * fm <= 1.75f) ? E - 8 : E - 7;
+  return max(-127, min(127, e));
+}
+
+// Nearest E4M3 code to y (|y| <= 448), ties to the even code.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  if (a < 0x3C800000u) {  // |y| < 2^-6: subnormal codes, steps of 2^-9 (the product is exact)
+    const float m = rintf(__uint_as_float(a) * 512.f);
+    return sign | static_cast<uint32_t>(m);  // 8 is the smallest normal, code 0x08
+  }
+  // Normal: keep 3 mantissa bits, round half to even; a carry moves into the
+  // exponent field.  Exponent bias 127 -> 7 is a subtraction of 120 << 3.
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+constexpr int kFp8RowThreads = 8;  // threads per (token, head) row, 8 values each
+
+__global__ __launch_bounds__(kThreads) void kv_append_fp8_kernel(const AppendParams p) {
+  constexpr int D = kHeadDim;
+  const int h = blockIdx.y;
+  const int H = p.num_heads;
+  const int P = p.page_size;
+  const int patch_tiles = (p.patch_tokens + kTile - 1) / kTile;
+  int tok0, ntok;
+  if (static_cast<int>(blockIdx.x) < patch_tiles) {
+    tok0 = blockIdx.x * kTile;
+    ntok = min(kTile, p.patch_tokens - tok0);
+  } else {
+    const int st = blockIdx.x - patch_tiles;
+    tok0 = p.patch_tokens + st * kTile;
+    ntok = min(kTile, p.patch_tokens + p.special_tokens - tok0);
+  }
+  if (ntok <= 0) return;
+  const int lane8 = threadIdx.x & (kFp8RowThreads - 1);
+  // Rows are processed by aligned groups of 8 lanes; every lane of a wave runs
+  // the same number of iterations, so the group reductions below see all 8.
+  for (int it = threadIdx.x / kFp8RowThreads; it < 2 * kTile; it += kThreads / kFp8RowThreads) {
+    const int t = it % kTile;
+    const bool is_v = it >= kTile;
+    const bool valid = t < ntok;
+    const int tok = tok0 + (valid ? t : 0);
+    const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_src : p.k_src) +
+                          (static_cast<size_t>(tok) * H + h) * D + lane8 * 8;
+    uint4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const uint4*>(src);
+    float x[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int m = 1; m < kFp8RowThreads; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kFp8RowThreads));
+    const int e = fp8_row_exponent(amax);
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i >> 2] |= e4m3_rne(ldexpf(x[i], -e)) << (8 * (i & 3));
+    if (!valid) continue;
+    const Dest dd = dest_of(p, tok);
+    const size_t row = (static_cast<size_t>(dd.page) * H + h) * P + dd.slot;
+    uint8_t* pool = static_cast<uint8_t*>(is_v ? p.v_pool : p.k_pool);
+    *reinterpret_cast<uint2*>(pool + row * D + lane8 * 8) = make_uint2(c[0], c[1]);
+    if (lane8 == 0) static_cast<int8_t*>(is_v ? p.v_exp : p.k_exp)[row] = static_cast<int8_t>(e);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t stream) {
@@ -116,8 +205,10 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t stream
   dim3 grid(tiles, p.num_heads);
   if (dtype == 0)
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
-  else
+  else if (dtype == 1)
     hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kv_append_fp8_kernel, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ int PageCache::validate(const kvc_config& c) {
   if (c.num_heads <= 0 || c.head_dim <= 0 || c.page_size <= 0 || c.patch_tokens <= 0) return KVC_ERR_INVALID_ARGUMENT;
   if (c.special_tokens < 0 || c.special_tokens > c.page_size) return KVC_ERR_INVALID_ARGUMENT;
   if (c.num_scale_units < 0 || c.max_units <= 0 || c.num_pages < 0) return KVC_ERR_INVALID_ARGUMENT;
-  if (c.dtype != KVC_DTYPE_BF16 && c.dtype != KVC_DTYPE_F32) return KVC_ERR_INVALID_ARGUMENT;
+  if (c.dtype != KVC_DTYPE_BF16 && c.dtype != KVC_DTYPE_F32 && c.dtype != KVC_DTYPE_FP8_E4M3)
+    return KVC_ERR_INVALID_ARGUMENT;
   if (c.special_packing != KVC_SPECIAL_FRAME_ALIGNED && c.special_packing != KVC_SPECIAL_CONTIGUOUS)
     return KVC_ERR_INVALID_ARGUMENT;
   return KVC_OK;

@@ -7,6 +7,7 @@ import pytest
 import synth
 from oracle import (E4M3_MAX, OracleCache, OracleConfig, bf16_bits_to_f64, dequantize_rows, e4m3_decode,
                     e4m3_encode, quantize_rows, row_exponent)
+from oracle.fp8 import e4m3_encode_array, row_exponents
 
 
 def _torch_codes(values):
@@ -77,3 +78,14 @@ def test_fp8_cache_gathers_the_quantised_history():
     sel = [hist_k[0][:P], hist_k[4][:P], hist_k[5][:P]] + [h[P:] for h in hist_k]
     ref = dequantize_rows(*quantize_rows(bf16_bits_to_f64(np.concatenate(sel))))
     assert (gk == ref.transpose(1, 0, 2)).all()
+
+
+def test_vectorised_forms_agree_with_the_scalar_steps():
+    rng = np.random.default_rng(3)
+    finite = sorted({abs(e4m3_decode(c)) for c in range(256) if not math.isnan(e4m3_decode(c))})
+    mids = [(a + b) / 2 for a, b in zip(finite, finite[1:])]
+    y = np.concatenate([rng.uniform(-448, 448, 5000), rng.uniform(-0.02, 0.02, 5000), finite, mids,
+                        [-x for x in mids], [0.0, -0.0]])
+    assert (e4m3_encode_array(y) == np.array([e4m3_encode(float(v)) for v in y], np.uint8)).all()
+    amax = np.concatenate([rng.uniform(1e-8, 1e8, 3000), [0.0, 448.0, 449.0, 448.0 * 2 ** 7]])
+    assert (row_exponents(amax) == np.array([row_exponent(float(a)) for a in amax])).all()
