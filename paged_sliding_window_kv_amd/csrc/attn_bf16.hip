@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -73,9 +74,15 @@ constexpr int DMA_PER_TILE = 16;    // 1 KiB global->LDS loads per tile (8 for K
 // open, and lgkmcnt(0) with the others left open.
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkmcnt0 = 0xC07F;
-// Headroom (log2 units) the running maximum may lag the true one before the
-// output accumulator is rescaled.
-constexpr float kRescaleSlack = 8.f;
+// A tile's probabilities are formed against the running maximum m as it
+// stands (no maximum of the tile is taken on the way).  They are accepted when
+// every lane's sum of them is at most kSumBound, which bounds each one; only
+// otherwise (a row whose scores outgrow m by several units, or m not yet set)
+// is the tile's maximum taken, O and the row sum rescaled, and the
+// probabilities formed again.  Values up to kSumBound are far from fp32 or
+// bf16 overflow, and the final division by the row sum is exact whichever
+// reference was used.
+constexpr float kSumBound = 65536.f;  // 2^16
 
 // 16-byte chunk c of LDS row r is stored at physical chunk c ^ swz(r).  Rows
 // are 128 bytes, so 16 consecutive rows read at the same logical chunk cover
@@ -179,24 +186,58 @@ __device__ __forceinline__ void cursor_next(const Src& src, int ee, Cursor& c) {
   }
 }
 
+// Lanes l, l^16, l^32 and l^48 hold the four 4-key groups of one query in the
+// 16x16 layout of the extra block; v_permlane16_swap pairs l with l^16 the way
+// v_permlane32_swap pairs l with l^32.
+__device__ __forceinline__ void pair16_values(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float quad_max(float x) {
+  float a, b;
+  pair16_values(x, a, b);
+  return pair_max(fmaxf(a, b));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  float a, b;
+  pair16_values(x, a, b);
+  return pair_sum(a + b);
+}
+
 // KV8: the pools hold FP8 (OCP E4M3) codes with per-(token, head) int8 row
 // exponents (layout in kvc.h).  The ring then stages the codes and exponents
 // of each tile (8,320 bytes), and after each pair's barrier the workgroup
-// converts the pair into the bf16 tile layout of `lds` (two tiles), with
-// v_cvt_scalef32_pk_bf16_fp8 applying 2^e; every later step is the bf16
-// kernel's.  The dequantised values are exactly bf16 numbers (3-bit
-// mantissas times powers of two).
+// converts the pair into two bf16 tiles with v_cvt_scalef32_pk_bf16_fp8
+// applying 2^e; every later step is the bf16 kernel's.  The dequantised
+// values are exactly bf16 numbers (3-bit mantissas times powers of two).
 template <int NB, bool XB, class Src, bool KV8 = false>
-__global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
-  static_assert(!XB || NB >= 4, "the extra block is shared by waves 0..3");
+__global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
+  static_assert(!XB || NB >= 2, "the extra block is shared by waves 0..3");
   const AttnParams& p = attn_base(src);
-  constexpr int ROWS = (NB + (XB ? 1 : 0)) * 32;
-  constexpr int LPT = (DMA_PER_TILE + NB - 1) / NB;  // direct loads per wave per tile
-  constexpr int NBUF = KV8 ? 2 : STAGES;            // bf16 tiles: the ring, or the converted pair
-  constexpr int STAGE8 = 2 * TILE_ELEMS + 2 * KT;   // FP8 stage: K codes, V codes, K exps, V exps
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint8_t lds8[KV8 ? STAGES : 1][KV8 ? STAGE8 : 16];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[ROWS * D];  // this tile's queries, swizzled rows
+  constexpr int W = 2 * NB;                             // waves: two per 32-row block
+  constexpr int ROWS = NB * 32 + (XB ? 16 : 0);
+  constexpr int LPT = (DMA_PER_TILE + W - 1) / W;       // direct loads per wave per tile
+  constexpr int TILE_BYTES = 2 * TILE_ELEMS * 2;        // K and V^T of one bf16 tile
+  constexpr int STAGE8 = 2 * TILE_ELEMS + 2 * KT;       // FP8 stage: K codes, V codes, K exps, V exps
+  constexpr int RING_BYTES = KV8 ? 2 * TILE_BYTES + STAGES * STAGE8 : STAGES * TILE_BYTES;
+  constexpr int Q_BYTES = ROWS * D * 2;
+  // Extra block: each quarter wave's O^T accumulator [4][16][64] (fp32)
+  // lives in LDS between steps, so it does not hold registers through the
+  // main products.
+  constexpr int XO_BYTES = XB ? 4 * 16 * 64 * 4 : 0;
+  // End of the kernel: the odd-tile waves' states [NB][34][64] and the extra
+  // block's quarter states [3][18][64] (fp32), over the idle ring.
+  constexpr int MERGE_BYTES = (NB * 34 + (XB ? 3 * 18 : 0)) * 64 * 4;
+  constexpr int SMEM = RING_BYTES + Q_BYTES + XO_BYTES > MERGE_BYTES ? RING_BYTES + Q_BYTES + XO_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  // bf16 tiles: the ring (STAGES tiles), or the converted pair (KV8)
+  uint16_t* const lds_t = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* const lds8 = smem + (KV8 ? 2 * TILE_BYTES : 0);  // FP8 stages
+  uint16_t* const lds_q = reinterpret_cast<uint16_t*>(smem + RING_BYTES);  // queries, swizzled rows
+  floatx4* const lds_xo = reinterpret_cast<floatx4*>(smem + RING_BYTES + Q_BYTES);  // [wave][db][lane]
 
   // ---- which (sequence, head, split, query tile) ----------------------------
   const int L = blockIdx.x;
@@ -223,17 +264,20 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   const int lane = tid & 63;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  // Own block: 32 rows per wave.  Extra block (XB): rows NB*32 .. NB*32+31 of
-  // the tile; waves 0..3 each take one 32-key quarter of every 128-key step.
-  const int wrow0 = row0 + wave * 32;
+  // Block blk = wave mod NB; waves below NB take the first tile of every
+  // 128-key step, the others the second.
+  const bool odd = wave >= NB;
+  const int blk = odd ? wave - NB : wave;
+  const int wrow0 = row0 + blk * 32;
   const bool active = wrow0 < qn;
   const int qrow = wrow0 + lr;
   const bool qvalid = qrow < qn;
+  // Extra block (XB): 16 rows NB*32 .. NB*32+15 of the tile, on 16x16x32
+  // products; waves 0..3 each take one 32-key quarter of every 128-key step.
   const int xrow0 = row0 + NB * 32;
   const bool xblock = XB && xrow0 < qn;  // workgroup-uniform
   const bool xactive = xblock && wave < 4;
-  const int xrow = xrow0 + lr;
-  const bool xvalid = xblock && xrow < qn;
+  const int c16 = lane & 15, g4 = lane >> 4;
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k_pool);
@@ -241,26 +285,32 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   const size_t page_stride = static_cast<size_t>(H) * P * D;  // elements per page (K or V)
   const size_t head_off = static_cast<size_t>(h) * P * D;
 
-  // ---- queries of the tile -> LDS (rows past the sequence are zero) ----------
+  // ---- queries of the tile -> LDS ---------------------------------------------
   // Q fragments (B operand of S^T = K Q^T: Q[row][16*st + 8*lh .. +7]) are read
-  // from here at every 128-key step rather than held in registers.
-  for (int c = tid; c < ROWS * 8; c += NB * 64) {
-    const int r = c >> 3, ch = c & 7;
-    const int row = row0 + r;
-    i32x4 v = {0, 0, 0, 0};
-    if (row < qn) v = *reinterpret_cast<const i32x4*>(qg + (static_cast<size_t>(q0 + row) * H + h) * D + ch * 8);
-    *reinterpret_cast<i32x4*>(lds_q + r * D + ((ch ^ swz(r)) << 3)) = v;
+  // from here at every step rather than held in registers.  The rows come by
+  // direct loads of 8 rows (1 KiB) each, issued before the first tiles so
+  // that both latencies overlap; the tile waits below cover them (loads
+  // complete in issue order), and the first ring barrier publishes lds_q and
+  // lds_xo.  Rows past the sequence repeat its last row: their outputs are
+  // never written.
+  for (int j = wave; j < ROWS / 8; j += W) {
+    const int r = j * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ swz(r);  // logical chunk held by physical chunk lane%8
+    const int row = min(row0 + r, qn - 1);
+    const uint16_t* gp = qg + (static_cast<size_t>(q0 + row) * H + h) * D + ch * 8;
+    __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_q + j * 512), 16, 0, 0);
   }
-  // Settle the Q loads before the ring starts, so that the wait counts below
-  // cover tile loads only (the first ring barrier publishes lds_q).
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  if (XB && xactive) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) lds_xo[(wave * 4 + db) * 64 + lane] = floatx4{};
+  }
 
   // ---- this wave's share of each tile's 16 direct loads -----------------------
   // Load `inst` of a tile fills 1 KiB = LDS positions 64*part .. 64*part+63 of
   // K (inst < 8) or V^T (inst >= 8); lane l fills position 64*part + l, i.e.
   // row 8*part + l/8, physical chunk l%8, which holds logical chunk
-  // (l%8) ^ swz(row).  Surplus slots (16 not divisible by NB) repeat the last
-  // load: identical bytes to identical addresses.
+  // (l%8) ^ swz(row).  Surplus slots (16 not divisible by the wave count)
+  // repeat the last load: identical bytes to identical addresses.
   int dma_goff[LPT], dma_loff[LPT];
   bool dma_v[LPT];
 #pragma unroll
@@ -300,10 +350,10 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
           // (the source goes in as const void*: a byte pointer there leaves the
           // host side of this instantiation without its launch stub)
           const void* gp = base + row0 * D + (dma8_off[j] & 4095) + lane * 16;
-          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds8[stage][0] + dma8_off[j]), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds8 + stage * STAGE8 + dma8_off[j]), 16, 0, 0);
         } else if (lane == 0) {
           const void* gp = base + codes_bytes + row0 + (dma8_off[j] - 8192 - (kind - 2) * KT);
-          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds8[stage][0] + dma8_off[j]), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds8 + stage * STAGE8 + dma8_off[j]), 16, 0, 0);
         }
       }
     } else {
@@ -312,7 +362,7 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
 #pragma unroll
       for (int j = 0; j < LPT; ++j) {
         const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
-        __builtin_amdgcn_global_load_lds(gp, (lds_void*)(&lds[stage][0][0] + dma_loff[j]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_t + stage * 2 * TILE_ELEMS + dma_loff[j]), 16, 0, 0);
       }
     }
   };
@@ -320,8 +370,14 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   // K rows keep their layout; V rows become V^T rows (dims) in the pool slot
   // order v_slot_pos with the chunk swizzle.  Keys past nk become zeros.
   auto convert = [&](int stage, int b, int nk) {
-    const uint8_t* st8 = &lds8[stage][0];
-    for (int it = tid; it < 2 * KT * 8; it += NB * 64) {
+    const uint8_t* st8 = lds8 + stage * STAGE8;
+    uint16_t* tk = lds_t + b * 2 * TILE_ELEMS;
+    // The per-thread addresses below are recomputed at every call (a few
+    // integer operations) rather than hoisted out of the key loop, where they
+    // would hold registers the products need.
+    int t0 = tid;
+    asm volatile("" : "+v"(t0));
+    for (int it = t0; it < 2 * KT * 8; it += W * 64) {
       const bool is_v = it >= KT * 8;
       const int r = (it >> 3) & (KT - 1), ch = it & 7;  // token, 8-dim chunk
       const uint2 w = *reinterpret_cast<const uint2*>(st8 + (is_v ? 4096 : 0) + r * D + ch * 8);
@@ -337,13 +393,13 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
       __builtin_memcpy(u, v2, sizeof u);
       if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
       if (!is_v) {
-        *reinterpret_cast<uint4*>(&lds[b][0][0] + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
+        *reinterpret_cast<uint4*>(tk + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
       } else {
         const int pos = v_slot_pos(r);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int row = ch * 8 + j;  // dim
-          lds[b][1][row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
+          tk[TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
               static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1)));
         }
       }
@@ -353,7 +409,7 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   // of a 16-key group sits at element sigma(k) of the group (sigma swaps the
   // middle two 4-slot groups); the 16-byte chunk is then swizzled by row.
   auto zero_tail = [&](uint16_t* lv, int nk) {
-    for (int it = tid; it < D * 16; it += NB * 64) {
+    for (int it = tid; it < D * 16; it += W * 64) {
       const int row = it >> 4, grp = it & 15;  // 4-key group in key order
       const int k0 = grp * 4;
       if (k0 + 4 <= nk) continue;
@@ -367,10 +423,11 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   };
 
   float m_run = -INFINITY;  // running max of scaled scores (log2 domain)
+  bool mset = false;        // m_run set (wave-uniform)
   float l_run = 0.f;        // this lane's partial row sum
   floatx16 o0 = {}, o1 = {};
-  float xm = -INFINITY, xl = 0.f;  // extra block, this wave's key quarters
-  floatx16 xo0 = {}, xo1 = {};
+  float xm = -INFINITY, xl = 0.f;  // extra block: this wave's key quarters
+  bool xset = false;
 
   // Tiles are consumed two at a time (128 keys per barrier).  Tile t lives in
   // ring stage t % STAGES; up to STAGES - 2 tiles beyond the current pair are
@@ -404,15 +461,15 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
       cursor_next(src, ee, cb);
       nkb = min(KT, cb.len - cb.kt * KT);
     }
-    const int sa = nc % STAGES, sb = (nc + 1) % STAGES;
-    const uint16_t* lka = lds[KV8 ? 0 : sa][0];
-    uint16_t* lva = lds[KV8 ? 0 : sa][1];
-    const uint16_t* lkb = lds[KV8 ? 1 : sb][0];
-    uint16_t* lvb = lds[KV8 ? 1 : sb][1];
+    const int sa = KV8 ? 0 : nc % STAGES, sb = KV8 ? 1 : (nc + 1) % STAGES;
+    uint16_t* const lka = lds_t + sa * 2 * TILE_ELEMS;
+    uint16_t* const lva = lka + TILE_ELEMS;
+    uint16_t* const lkb = lds_t + sb * 2 * TILE_ELEMS;
+    uint16_t* const lvb = lkb + TILE_ELEMS;
     if constexpr (KV8) {
       // Everyone is done with the previous pair's bf16 tiles (barrier above).
-      convert(sa, 0, nka);
-      if (two) convert(sb, 1, nkb);
+      convert(nc % STAGES, 0, nka);
+      if (two) convert((nc + 1) % STAGES, 1, nkb);
       __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
       __builtin_amdgcn_s_barrier();
     } else if (nka < KT || (two && nkb < KT)) {
@@ -422,44 +479,36 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
       __builtin_amdgcn_s_barrier();
     }
 
-    if (active) {
-      bf16x8 qf[4];
+    const int nk = odd ? nkb : nka;  // this wave's tile (nkb = 0 without a second tile)
+    if (active && nk > 0) {
+      const uint16_t* lk = odd ? lkb : lka;
+      const uint16_t* lv = odd ? lvb : lva;
+      // Scores of the tile (keys 0..31 then 32..63, four K fragments live at
+      // a time), keys past nk set to -inf.
+      auto scores = [&](floatx16& s0, floatx16& s1) {
+        bf16x8 qf[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) qf[st] = lds_frag(lds_q, wave * 32 + lr, 2 * st + lh);
-      // Operand fragments of a product group are all read from LDS before its
-      // first MFMA, so the matrix pipe is not left waiting on each read.
-      auto qk = [&](const uint16_t* lk, floatx16& s0, floatx16& s1) {
-        bf16x8 ka[4], kb[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          ka[st] = lds_frag(lk, lr, 2 * st + lh);
-          kb[st] = lds_frag(lk, 32 + lr, 2 * st + lh);
-        }
+        for (int st = 0; st < 4; ++st) qf[st] = lds_frag(lds_q, blk * 32 + lr, 2 * st + lh);
         s0 = floatx16{};
         s1 = floatx16{};
+        __builtin_amdgcn_s_setprio(1);
+        {
+          bf16x8 kf[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st], qf[st], s1, 0, 0, 0);
-        }
-      };
-      auto pv = [&](const floatx16& s0, const floatx16& s1, const uint16_t* lv) {
-        bf16x8 va[4], vb[4];
+          for (int st = 0; st < 4; ++st) kf[st] = lds_frag(lk, lr, 2 * st + lh);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          va[t] = lds_frag(lv, lr, 2 * t + lh);
-          vb[t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+          for (int st = 0; st < 4; ++st) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s0, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          bf16x8 kf[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 pb = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb, o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[t], pb, o1, 0, 0, 0);
+          for (int st = 0; st < 4; ++st) kf[st] = lds_frag(lk, 32 + lr, 2 * st + lh);
+#pragma unroll
+          for (int st = 0; st < 4; ++st) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s1, 0, 0, 0);
         }
-      };
-      // Softmax update of one tile's scores, in place (scores -> probabilities).
-      auto soft = [&](floatx16& s0, floatx16& s1, int nk, bool full) {
-        if (!full && nk < KT) {
+        __builtin_amdgcn_s_setprio(0);
+        if (nk < KT) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
@@ -467,126 +516,135 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
             if (key + 32 >= nk) s1[r] = -INFINITY;
           }
         }
-        const float mx = pair_max(tile_max(s0, s1)) * sl2;
-        // The reference maximum only moves when a row's maximum exceeds it by
-        // more than kRescaleSlack (log2 units): probabilities stay <= 2^slack,
-        // far from fp32 or bf16 overflow, and the final division by the row
-        // sum is exact whichever reference was used.
-        if (__any(mx > m_run + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            o0[r] *= alpha;
-            o1[r] *= alpha;
-          }
-        }
+      };
+      // Probabilities against the running maximum, in place; returns this
+      // lane's sum of them.
+      auto probs = [&](floatx16& s0, floatx16& s1) {
         const float nm = -m_run;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, nm));
           s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, nm));
         }
-        l_run += tile_sum(s0, s1);
+        return tile_sum(s0, s1);
       };
-      floatx16 a0, a1, b0, b1;
-      if (two && nka == KT && nkb == KT) {
-        // Full pair: one straight-line block with a single softmax update for
-        // all 128 keys.  Waves w and w+4 share a SIMD; the upper half takes the
-        // pair in the opposite order so that one wave's softmax arithmetic
-        // tends to run under the other's products.
-        const bool rev = (wave & 4) != 0;
-        const uint16_t* k1 = rev ? lkb : lka;
-        const uint16_t* k2 = rev ? lka : lkb;
-        const uint16_t* v1 = rev ? lvb : lva;
-        const uint16_t* v2 = rev ? lva : lvb;
-        __builtin_amdgcn_s_setprio(1);
-        qk(k1, a0, a1);
-        qk(k2, b0, b1);
-        __builtin_amdgcn_s_setprio(0);
-        const float mx = pair_max(fmaxf(tile_max(a0, a1), tile_max(b0, b1))) * sl2;
-        if (__any(mx > m_run + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            o0[r] *= alpha;
-            o1[r] *= alpha;
-          }
-        }
-        const float nm = -m_run;
+      floatx16 s0, s1;
+      scores(s0, s1);
+      if (!mset) {  // this wave's first tile: start from its exact maximum
+        m_run = pair_max(tile_max(s0, s1)) * sl2;
+        mset = true;
+      }
+      float lt = probs(s0, s1);
+      if (__any(!(lt <= kSumBound))) {
+        // Rare: take the tile's maximum (from the scores formed again: the K
+        // tile is still in LDS) and rescale.
+        scores(s0, s1);
+        const float mx = pair_max(tile_max(s0, s1)) * sl2;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          a0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a0[r], sl2, nm));
-          a1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[r], sl2, nm));
-          b0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(b0[r], sl2, nm));
-          b1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(b1[r], sl2, nm));
+          o0[r] *= alpha;
+          o1[r] *= alpha;
         }
-        l_run += tile_sum(a0, a1) + tile_sum(b0, b1);
-        pv(a0, a1, v1);
-        pv(b0, b1, v2);
-      } else {
-        qk(lka, a0, a1);
-        soft(a0, a1, nka, false);
-        pv(a0, a1, lva);
-        if (two) {
-          qk(lkb, b0, b1);
-          soft(b0, b1, nkb, false);
-          pv(b0, b1, lvb);
-        }
+        lt = probs(s0, s1);
+      }
+      l_run += lt;
+      // V fragments are read only now: reading them during the softmax would
+      // keep K, V and the scores live together (other waves hide the wait).
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 va[4], vb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        va[t] = lds_frag(lv, lr, 2 * t + lh);
+        vb[t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 pb = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb, o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[t], pb, o1, 0, 0, 0);
       }
     }
 
     if (XB && xactive) {
-      // Extra block: this wave's 32-key quarter of the 128-key step.
-      const int tile = wave >> 1, kb = wave & 1;
-      const int nkt = tile ? (two ? nkb : 0) : nka;
-      if (nkt > 32 * kb) {
+      // Extra block: this wave's 32-key quarter kq..kq+31 of the step, as two
+      // 16-key blocks of S^T (16 keys x 16 queries, v_mfma_f32_16x16x32_bf16).
+      // Block c holds keys kq + 8c + {0..7, 16..23}, so that the 4-key groups
+      // lane group g4 receives are exactly the two halves of V^T chunk
+      // kq/8 + g4 (pool slot order) and P feeds O^T = V^T P^T unchanged.
+      const int tile = wave >> 1, kq = 32 * (wave & 1);
+      const int nkt = tile ? nkb : nka;
+      if (nkt > kq) {
         const uint16_t* lk = tile ? lkb : lka;
         const uint16_t* lv = tile ? lvb : lva;
-        floatx16 s = {};
-        __builtin_amdgcn_s_setprio(1);
+        const int kr = kq + (c16 & 7) + 16 * (c16 >> 3);
+        auto xscores = [&](floatx4& sa0, floatx4& sa1) {
+          sa0 = floatx4{};
+          sa1 = floatx4{};
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lk, 32 * kb + lr, 2 * st + lh),
-                                                      lds_frag(lds_q, NB * 32 + lr, 2 * st + lh), s, 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
-        if (nkt < 32 * kb + 32) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kb + (r >> 2) * 8 + lh * 4 + (r & 3);
-            if (key >= nkt) s[r] = -INFINITY;
+          for (int ds = 0; ds < 2; ++ds) {
+            const bf16x8 qx = lds_frag(lds_q, NB * 32 + c16, 4 * ds + g4);
+            sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(lk, kr, 4 * ds + g4), qx, sa0, 0, 0, 0);
+            sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(lk, kr + 8, 4 * ds + g4), qx, sa1, 0, 0, 0);
           }
+          __builtin_amdgcn_s_setprio(0);
+          if (nkt < kq + 32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int idx = 4 * g4 + i;
+              const int key = kq + (idx & 7) + 16 * (idx >> 3);
+              if (key >= nkt) sa0[i] = -INFINITY;
+              if (key + 8 >= nkt) sa1[i] = -INFINITY;
+            }
+          }
+        };
+        auto xmax = [&](const floatx4& sa0, const floatx4& sa1) {
+          return quad_max(fmaxf(fmaxf(fmaxf(sa0[0], sa0[1]), fmaxf(sa0[2], sa0[3])),
+                                fmaxf(fmaxf(sa1[0], sa1[1]), fmaxf(sa1[2], sa1[3])))) * sl2;
+        };
+        floatx8 pf;
+        auto xprobs = [&](const floatx4& sa0, const floatx4& sa1) {
+          const float nm = -xm;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa0[i], sl2, nm));
+            pf[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa1[i], sl2, nm));
+          }
+          return ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+        };
+        floatx4 sa0, sa1;
+        xscores(sa0, sa1);
+        if (!xset) {
+          xm = xmax(sa0, sa1);
+          xset = true;
         }
-        const float mx = pair_max(half_max(s)) * sl2;
-        if (__any(mx > xm + kRescaleSlack)) {
-          const float m_new = fmaxf(xm, mx);
-          const float alpha = __builtin_amdgcn_exp2f(xm - m_new);
+        float xlt = xprobs(sa0, sa1);
+        floatx4 xo[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) xo[db] = lds_xo[(wave * 4 + db) * 64 + lane];
+        if (__any(!(xlt <= kSumBound))) {
+          xscores(sa0, sa1);
+          const float m_new = fmaxf(xm, xmax(sa0, sa1));
+          const float alpha = xm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm - m_new);
           xm = m_new;
           xl *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            xo0[r] *= alpha;
-            xo1[r] *= alpha;
-          }
+          for (int db = 0; db < 4; ++db) xo[db] *= alpha;
+          xlt = xprobs(sa0, sa1);
         }
-        const float nm = -xm;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, nm));
-        xl += half_sum(s);
+        xl += xlt;
+        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = to_bf16x8(s, 8 * ks);
-          const int ch = 2 * (2 * kb + ks) + lh;
-          xo0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lv, lr, ch), pb, xo0, 0, 0, 0);
-          xo1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lv, 32 + lr, ch), pb, xo1, 0, 0, 0);
-        }
+        for (int db = 0; db < 4; ++db)
+          xo[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(lv, db * 16 + c16, kq / 8 + g4), pb, xo[db], 0, 0, 0);
         __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) lds_xo[(wave * 4 + db) * 64 + lane] = xo[db];
       }
     }
     for (int s = 0; s < 2 && lc.e < ee; ++s) {
@@ -600,109 +658,133 @@ __global__ __launch_bounds__(NB * 64) void attn_bf16_kernel(const Src src) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  // Writes one 32-row block: normalised O (bf16) and lse, or the split's
-  // partial O (fp32) and lse.  m is the running maximum, ltot the row sum.
-  auto write_block = [&](int row, bool valid, const floatx16& a0, const floatx16& a1, float m, float ltot) {
+  // Writes one row's result: normalised O (bf16) and lse, or the split's
+  // partial O (fp32) and lse.  `get(j)` returns the unnormalised O of dims
+  // d0[j/4] + j%4 (4 dims per run, `runs` runs); m is the maximum, ltot the
+  // row sum; the lse is written by lanes with `lse_lane`.
+  auto write_row = [&](int row, auto get, const int* d0, auto runs_c, float m, float ltot, bool lse_lane) {
+    constexpr int runs = decltype(runs_c)::value;
     const bool empty = !(ltot > 0.f);
     const float inv = empty ? 0.f : 1.f / ltot;
     const float lse_nat = empty ? -INFINITY : (m + __log2f(ltot)) * 0.69314718055994530942f;
-    if (!valid) return;
     const size_t orow = static_cast<size_t>(q0 + row) * H + h;
     if (p.num_splits == 1) {
       uint16_t* og = static_cast<uint16_t*>(p.o) + orow * D;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int r4 = 0; r4 < runs; ++r4) {
+        floatx4 f;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          floatx4 f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) f[j] = (db ? a1 : a0)[r4 * 4 + j] * inv;
-          *reinterpret_cast<bf16x4*>(og + db * 32 + r4 * 8 + lh * 4) = __builtin_convertvector(f, bf16x4);
-        }
+        for (int j = 0; j < 4; ++j) f[j] = get(r4 * 4 + j) * inv;
+        *reinterpret_cast<bf16x4*>(og + d0[r4]) = __builtin_convertvector(f, bf16x4);
       }
-      if (p.lse && lh == 0) p.lse[orow] = lse_nat;
+      if (p.lse && lse_lane) p.lse[orow] = lse_nat;
     } else {
       float* po = p.part_o + (static_cast<size_t>(split) * p.total_q * H + orow) * D;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int r4 = 0; r4 < runs; ++r4) {
+        floatx4 f;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          floatx4 f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) f[j] = (db ? a1 : a0)[r4 * 4 + j] * inv;
-          *reinterpret_cast<floatx4*>(po + db * 32 + r4 * 8 + lh * 4) = f;
-        }
+        for (int j = 0; j < 4; ++j) f[j] = get(r4 * 4 + j) * inv;
+        *reinterpret_cast<floatx4*>(po + d0[r4]) = f;
       }
-      if (lh == 0) p.part_lse[static_cast<size_t>(split) * p.total_q * H + orow] = lse_nat;
+      if (lse_lane) p.part_lse[static_cast<size_t>(split) * p.total_q * H + orow] = lse_nat;
     }
   };
 
-  if (XB && xblock) {
-    // Combine the extra block's four key-quarter states: waves 1..3 hand
-    // theirs to wave 0 through LDS (the ring is idle: every issued tile has
-    // been consumed, and the barrier below orders the reuse).
-    float* xbuf = reinterpret_cast<float*>(&lds[0][0][0]);  // [3][64 dims][32 rows]
-    float* xms = xbuf + 3 * 64 * 32;                        // [3][32]
-    float* xls = xms + 3 * 32;                              // [3][32]
-    const float xl_tot = pair_sum(xl);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-    __builtin_amdgcn_s_barrier();
-    if (wave >= 1 && wave < 4) {
-      float* b = xbuf + (wave - 1) * 64 * 32;
+  // Combine the two tile-parity states of each block, and the extra block's
+  // four quarter states, through LDS over the idle ring: every issued tile has
+  // been consumed, and the barrier orders the reuse.
+  float* const mbuf = reinterpret_cast<float*>(smem);  // [NB][34][64]
+  float* const xbuf = mbuf + NB * 34 * 64;             // [3][18][64]
+  floatx4 xo[4] = {};
+  if (XB && xactive) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = (r >> 2) * 8 + lh * 4 + (r & 3);
-        b[d * 32 + lr] = xo0[r];
-        b[(32 + d) * 32 + lr] = xo1[r];
-      }
-      if (lh == 0) {
-        xms[(wave - 1) * 32 + lr] = xm;
-        xls[(wave - 1) * 32 + lr] = xl_tot;
-      }
+    for (int db = 0; db < 4; ++db) xo[db] = lds_xo[(wave * 4 + db) * 64 + lane];
+  }
+  // (vmcnt: the query loads are still in flight when a split has no tiles)
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+  __builtin_amdgcn_s_barrier();
+  if (odd && active) {
+    float* b = mbuf + blk * 34 * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      b[r * 64] = o0[r];
+      b[(16 + r) * 64] = o1[r];
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-    __builtin_amdgcn_s_barrier();
-    if (wave == 0) {
-      float mw[3], lw[3];
-      float M = xm;
+    b[32 * 64] = m_run;
+    b[33 * 64] = l_run;
+  }
+  if (XB && xactive && wave >= 1) {
+    float* b = xbuf + (wave - 1) * 18 * 64 + lane;
 #pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        mw[w] = xms[w * 32 + lr];
-        lw[w] = xls[w * 32 + lr];
-        M = fmaxf(M, mw[w]);
-      }
-      const float c0 = xm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm - M);
-      float cw[3];
-      float Lt = xl_tot * c0;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        cw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-        Lt += lw[w] * cw[w];
-      }
+      for (int i = 0; i < 4; ++i) b[(db * 4 + i) * 64] = xo[db][i];
+    b[16 * 64] = xm;
+    b[17 * 64] = xl;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+  __builtin_amdgcn_s_barrier();
+  if (!odd && active) {
+    const float* b = mbuf + blk * 34 * 64 + lane;
+    const float m1 = b[32 * 64], l1 = b[33 * 64];
+    const float M = fmaxf(m_run, m1);
+    const float c0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    const float c1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = (r >> 2) * 8 + lh * 4 + (r & 3);
-        float a = xo0[r] * c0, b = xo1[r] * c0;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) {
-          a = __builtin_fmaf(xbuf[(w * 64 + d) * 32 + lr], cw[w], a);
-          b = __builtin_fmaf(xbuf[(w * 64 + 32 + d) * 32 + lr], cw[w], b);
-        }
-        xo0[r] = a;
-        xo1[r] = b;
-      }
-      write_block(xrow, xvalid, xo0, xo1, M, Lt);
+    for (int r = 0; r < 16; ++r) {
+      o0[r] = __builtin_fmaf(b[r * 64], c1, o0[r] * c0);
+      o1[r] = __builtin_fmaf(b[(16 + r) * 64], c1, o1[r] * c0);
+    }
+    const float l_tot = pair_sum(__builtin_fmaf(l1, c1, l_run * c0));
+    if (qvalid) {
+      // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
+      const int d0[8] = {4 * lh, 8 + 4 * lh, 16 + 4 * lh, 24 + 4 * lh, 32 + 4 * lh, 40 + 4 * lh, 48 + 4 * lh, 56 + 4 * lh};
+      write_row(qrow, [&](int j) { return j < 16 ? o0[j] : o1[j - 16]; }, d0, std::integral_constant<int, 8>{}, M, l_tot, lh == 0);
     }
   }
-  if (!active) return;
-  const float l_tot = pair_sum(l_run);
-  write_block(qrow, qvalid, o0, o1, m_run, l_tot);
+  if (XB && xactive && wave == 0) {
+    float mw[3], lw[3];
+    float M = xm;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      mw[w] = xbuf[(w * 18 + 16) * 64 + lane];
+      lw[w] = xbuf[(w * 18 + 17) * 64 + lane];
+      M = fmaxf(M, mw[w]);
+    }
+    const float c0 = xm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm - M);
+    float cw[3];
+    float lt = xl * c0;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      cw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+      lt = __builtin_fmaf(lw[w], cw[w], lt);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = xo[db][i] * c0;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) a = __builtin_fmaf(xbuf[(w * 18 + db * 4 + i) * 64 + lane], cw[w], a);
+        xo[db][i] = a;
+      }
+    const float l_tot = quad_sum(lt);
+    const int xrow = xrow0 + c16;
+    if (xrow < qn) {
+      // 16x16 accumulator: element i of xo[db] is dim 16*db + 4*g4 + i.
+      const int d0[4] = {4 * g4, 16 + 4 * g4, 32 + 4 * g4, 48 + 4 * g4};
+      write_row(xrow, [&](int j) { return xo[j >> 2][j & 3]; }, d0, std::integral_constant<int, 4>{}, M, l_tot, g4 == 0);
+    }
+  }
 }
 
 }  // namespace
 
-// waves <= 8: that many 32-row blocks; 9: eight waves plus the shared extra block.
-int attn_bf16_rows_per_tile(int waves) { return waves * 32; }
+// blocks <= 8: that many 32-row blocks; 9: eight blocks plus the shared 16-row
+// extra block.
+int attn_bf16_rows_per_tile(int blocks) { return blocks <= 8 ? blocks * 32 : 8 * 32 + 16; }
 
 template <bool KV8, class Src>
 static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
@@ -711,7 +793,7 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
   switch (waves) {
 #define KVC_CASE(W)                                                                                    \
   case W:                                                                                              \
-    hipLaunchKernelGGL((attn_bf16_kernel<W, false, Src, KV8>), grid, dim3(W * 64), 0, stream, src); \
+    hipLaunchKernelGGL((attn_bf16_kernel<W, false, Src, KV8>), grid, dim3(W * 128), 0, stream, src); \
     break;
     KVC_CASE(1)
     KVC_CASE(2)
@@ -723,7 +805,7 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
     KVC_CASE(8)
 #undef KVC_CASE
     case 9:
-      hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 64), 0, stream, src);
+      hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 128), 0, stream, src);
       break;
     default:
       return hipErrorInvalidValue;

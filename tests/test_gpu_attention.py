@@ -136,6 +136,37 @@ def test_multi_sequence_ragged(dtype):
                 assert (to_f64(o[a:b]) == 0).all()
 
 
+@pytest.mark.parametrize("qn", [1, 32, 33, 100, 224, 256, 257, 262, 271, 272, 273, 288, 289, 545])
+def test_query_counts_across_tile_shapes(qn):
+    """One sequence whose query count walks through every workgroup shape: 1..8
+    32-row blocks, the 272-row tile with its 16-row extra block, and a second
+    query tile; keys from ragged pages, with and without key splits."""
+    import torch
+    from paged_sliding_window_kv_amd import paged_attention
+    log(f"query count {qn}")
+    rng = np.random.default_rng(1000 + qn)
+    H, P, N = 2, 256, 16
+    ids, lens, kv = _random_tables(rng, [7], N, P)
+    qo = np.array([0, qn], np.int32)
+    kpool = synth.normal_tokens(4, 0, qn, 1, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    vpool = synth.normal_tokens(4, 0, qn, 2, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    q = synth.normal_tokens(4, 0, qn, 0, qn, H, 64, "bf16")
+    kd = to_dev(kpool, "bf16")
+    vd = to_dev(v_pool_device_layout(vpool), "bf16")
+    pos = torch.from_numpy(v_positions(P)).cuda()
+    for p_, n in zip(ids, lens):
+        kd[p_, :, n:] = float("nan")
+        vd[p_][:, :, pos[n:]] = float("nan")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    gk = np.concatenate([kpool[p_, :, :n] for p_, n in zip(ids, lens)], axis=1)
+    gv = np.concatenate([vpool[p_, :, :n] for p_, n in zip(ids, lens)], axis=1)
+    ro, rl = attention_f64(bits_f64(q), bits_f64(gk), bits_f64(gv))
+    for splits in (1, 3):
+        o, lse = paged_attention(to_dev(q, "bf16"), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
+                                 max_qo_len=qn, max_kv_pages=7, num_splits=splits)
+        check_attention(o, lse, ro, rl, "bf16", f"q={qn} splits={splits} Lk={gk.shape[1]}")
+
+
 def test_page_order_and_placement_invariance():
     import torch
     from paged_sliding_window_kv_amd import paged_attention
