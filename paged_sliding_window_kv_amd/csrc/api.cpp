@@ -52,9 +52,9 @@ bool device_shapes_ok(const kvc_config& c) {
 constexpr int kXcds = 8;
 
 int choose_waves(const paged_attn_args& a) {
-  // Up to 256 query rows: one wave per 32 rows, all in one workgroup, so each
-  // key tile is read once per split.  Beyond that: 288-row workgroups (eight
-  // waves plus the block their first four share), returned as 9.
+  // Up to 256 query rows: one 32-row block per 32 rows (two waves each), all
+  // in one workgroup, so each key tile is read once per split.  Beyond that:
+  // 272-row workgroups (eight blocks plus a 16-row extra block), returned as 9.
   if (a.max_qo_len <= 256) return std::max(1, (a.max_qo_len + 31) / 32);
   return 9;
 }

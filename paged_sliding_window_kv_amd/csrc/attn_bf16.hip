@@ -9,18 +9,27 @@
 // maximum and sum per query, so no score matrix is stored.
 //
 // Mapping to the hardware
-//  * One workgroup = NB waves covering NB*32 query rows of one (sequence,
-//    head, key split), each wave owning 32 rows.  The tile's queries sit in
-//    LDS; Q fragments are re-read there every 128-key step.  Variant NB = 8 + extra block covers
-//    288 rows (the 262 queries of a frame fit one workgroup): the ninth
-//    32-row block is shared by waves 0..3, each taking one 32-key quarter of
-//    every 128-key step, so each SIMD carries the same load (2.25 blocks);
-//    their four partial softmax states are merged through LDS at the end.
-//  * Keys are consumed 128 at a time (two 64-key tiles per barrier); the
-//    online softmax still updates per 64-key tile.
+//  * One workgroup = 2*NB waves covering NB*32 query rows of one (sequence,
+//    head, key split).  Waves w and w+NB own the same 32 rows: each 128-key
+//    step (two 64-key tiles per barrier) gives the first tile to wave w and
+//    the second to wave w+NB, each with its own online-softmax state; the
+//    two states are merged through LDS at the end.  With NB = 8 that is 16
+//    waves, four per SIMD, so one wave's products can run under another's
+//    softmax arithmetic.  The tile's queries sit in LDS (loaded by direct
+//    loads with the first key tiles); Q fragments are re-read there every
+//    step rather than held in registers.
+//  * Variant NB = 8 + extra block covers 272 rows (the 262 queries of a
+//    frame fit one workgroup): the 16-row extra block runs on
+//    v_mfma_f32_16x16x32_bf16, waves 0..3 (one per SIMD) each taking one
+//    32-key quarter of every step; its accumulators wait in LDS between
+//    steps, and the four quarter states are merged at the end.
+//  * The online softmax forms each tile's probabilities against the running
+//    maximum as it stands and accepts them when the lane's sum is bounded
+//    (see kSumBound); the tile maximum is taken only on a wave's first tile
+//    and in the rare case a sum exceeds the bound.
 //  * Scores are formed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS, B = 16 dims x
-//    32 queries from registers.  In the 32x32 accumulator each lane then
+//    v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims, B = 16 dims x 32
+//    queries, both from LDS.  In the 32x32 accumulator each lane then
 //    holds 16 scores of a single query, so the row maximum and row sum are
 //    in-lane reductions (shallow trees) plus one v_permlane32_swap between
 //    lane l and lane l + 32.
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
   const int P = p.page_size;
   const float sl2 = p.scale_log2;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 31;
   const int lh = lane >> 5;
@@ -691,91 +700,102 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
     }
   };
 
-  // Combine the two tile-parity states of each block, and the extra block's
-  // four quarter states, through LDS over the idle ring: every issued tile has
-  // been consumed, and the barrier orders the reuse.
-  float* const mbuf = reinterpret_cast<float*>(smem);  // [NB][34][64]
-  float* const xbuf = mbuf + NB * 34 * 64;             // [3][18][64]
-  floatx4 xo[4] = {};
-  if (XB && xactive) {
+  // The lane indices are formed again here (from an opaque copy of the
+  // thread index) rather than kept alive across the key loop.
+  int t_end = tid;
+  asm volatile("" : "+v"(t_end));
+  {
+    const int lane = t_end & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const int qrow = wrow0 + lr;
+    const bool qvalid = qrow < qn;
+    // Combine the two tile-parity states of each block, and the extra block's
+    // four quarter states, through LDS over the idle ring: every issued tile has
+    // been consumed, and the barrier orders the reuse.
+    float* const mbuf = reinterpret_cast<float*>(smem);  // [NB][34][64]
+    float* const xbuf = mbuf + NB * 34 * 64;             // [3][18][64]
+    floatx4 xo[4] = {};
+    if (XB && xactive) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) xo[db] = lds_xo[(wave * 4 + db) * 64 + lane];
-  }
-  // (vmcnt: the query loads are still in flight when a split has no tiles)
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-  __builtin_amdgcn_s_barrier();
-  if (odd && active) {
-    float* b = mbuf + blk * 34 * 64 + lane;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      b[r * 64] = o0[r];
-      b[(16 + r) * 64] = o1[r];
+      for (int db = 0; db < 4; ++db) xo[db] = lds_xo[(wave * 4 + db) * 64 + lane];
     }
-    b[32 * 64] = m_run;
-    b[33 * 64] = l_run;
-  }
-  if (XB && xactive && wave >= 1) {
-    float* b = xbuf + (wave - 1) * 18 * 64 + lane;
+    // (vmcnt: the query loads are still in flight when a split has no tiles)
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    __builtin_amdgcn_s_barrier();
+    if (odd && active) {
+      float* b = mbuf + blk * 34 * 64 + lane;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b[(db * 4 + i) * 64] = xo[db][i];
-    b[16 * 64] = xm;
-    b[17 * 64] = xl;
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-  __builtin_amdgcn_s_barrier();
-  if (!odd && active) {
-    const float* b = mbuf + blk * 34 * 64 + lane;
-    const float m1 = b[32 * 64], l1 = b[33 * 64];
-    const float M = fmaxf(m_run, m1);
-    const float c0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-    const float c1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      o0[r] = __builtin_fmaf(b[r * 64], c1, o0[r] * c0);
-      o1[r] = __builtin_fmaf(b[(16 + r) * 64], c1, o1[r] * c0);
-    }
-    const float l_tot = pair_sum(__builtin_fmaf(l1, c1, l_run * c0));
-    if (qvalid) {
-      // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
-      const int d0[8] = {4 * lh, 8 + 4 * lh, 16 + 4 * lh, 24 + 4 * lh, 32 + 4 * lh, 40 + 4 * lh, 48 + 4 * lh, 56 + 4 * lh};
-      write_row(qrow, [&](int j) { return j < 16 ? o0[j] : o1[j - 16]; }, d0, std::integral_constant<int, 8>{}, M, l_tot, lh == 0);
-    }
-  }
-  if (XB && xactive && wave == 0) {
-    float mw[3], lw[3];
-    float M = xm;
-#pragma unroll
-    for (int w = 0; w < 3; ++w) {
-      mw[w] = xbuf[(w * 18 + 16) * 64 + lane];
-      lw[w] = xbuf[(w * 18 + 17) * 64 + lane];
-      M = fmaxf(M, mw[w]);
-    }
-    const float c0 = xm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm - M);
-    float cw[3];
-    float lt = xl * c0;
-#pragma unroll
-    for (int w = 0; w < 3; ++w) {
-      cw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-      lt = __builtin_fmaf(lw[w], cw[w], lt);
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a = xo[db][i] * c0;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) a = __builtin_fmaf(xbuf[(w * 18 + db * 4 + i) * 64 + lane], cw[w], a);
-        xo[db][i] = a;
+      for (int r = 0; r < 16; ++r) {
+        b[r * 64] = o0[r];
+        b[(16 + r) * 64] = o1[r];
       }
-    const float l_tot = quad_sum(lt);
-    const int xrow = xrow0 + c16;
-    if (xrow < qn) {
-      // 16x16 accumulator: element i of xo[db] is dim 16*db + 4*g4 + i.
-      const int d0[4] = {4 * g4, 16 + 4 * g4, 32 + 4 * g4, 48 + 4 * g4};
-      write_row(xrow, [&](int j) { return xo[j >> 2][j & 3]; }, d0, std::integral_constant<int, 4>{}, M, l_tot, g4 == 0);
+      b[32 * 64] = m_run;
+      b[33 * 64] = l_run;
+    }
+    if (XB && xactive && wave >= 1) {
+      float* b = xbuf + (wave - 1) * 18 * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[(db * 4 + i) * 64] = xo[db][i];
+      b[16 * 64] = xm;
+      b[17 * 64] = xl;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    __builtin_amdgcn_s_barrier();
+    if (!odd && active) {
+      const float* b = mbuf + blk * 34 * 64 + lane;
+      const float m1 = b[32 * 64], l1 = b[33 * 64];
+      const float M = fmaxf(m_run, m1);
+      const float c0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float c1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o0[r] = __builtin_fmaf(b[r * 64], c1, o0[r] * c0);
+        o1[r] = __builtin_fmaf(b[(16 + r) * 64], c1, o1[r] * c0);
+      }
+      const float l_tot = pair_sum(__builtin_fmaf(l1, c1, l_run * c0));
+      if (qvalid) {
+        // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
+        const int d0[8] = {4 * lh, 8 + 4 * lh, 16 + 4 * lh, 24 + 4 * lh, 32 + 4 * lh, 40 + 4 * lh, 48 + 4 * lh, 56 + 4 * lh};
+        write_row(qrow, [&](int j) { return j < 16 ? o0[j] : o1[j - 16]; }, d0, std::integral_constant<int, 8>{}, M, l_tot, lh == 0);
+      }
+    }
+    if (XB && xactive && wave == 0) {
+      float mw[3], lw[3];
+      float M = xm;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        mw[w] = xbuf[(w * 18 + 16) * 64 + lane];
+        lw[w] = xbuf[(w * 18 + 17) * 64 + lane];
+        M = fmaxf(M, mw[w]);
+      }
+      const float c0 = xm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(xm - M);
+      float cw[3];
+      float lt = xl * c0;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        cw[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        lt = __builtin_fmaf(lw[w], cw[w], lt);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = xo[db][i] * c0;
+#pragma unroll
+          for (int w = 0; w < 3; ++w) a = __builtin_fmaf(xbuf[(w * 18 + db * 4 + i) * 64 + lane], cw[w], a);
+          xo[db][i] = a;
+        }
+      const float l_tot = quad_sum(lt);
+      const int xrow = xrow0 + c16;
+      if (xrow < qn) {
+        // 16x16 accumulator: element i of xo[db] is dim 16*db + 4*g4 + i.
+        const int d0[4] = {4 * g4, 16 + 4 * g4, 32 + 4 * g4, 48 + 4 * g4};
+        write_row(xrow, [&](int j) { return xo[j >> 2][j & 3]; }, d0, std::integral_constant<int, 4>{}, M, l_tot, g4 == 0);
+      }
     }
   }
 }
