@@ -7,9 +7,9 @@
 // Parts with lse_i = -inf (no keys) carry zero weight; if every part is empty
 // the output is 0 and lse is -inf.
 //
-// One thread per (row, head, dim); 64 consecutive threads read one part's
-// 256-byte row, so every access is coalesced, and each thread keeps eight
-// parts' loads in flight at once.
+// One thread per (row, head, 4 dims): a wave covers 4 (row, head) pairs, so
+// each part's load instruction reads 1 KiB of contiguous partials, and each
+// thread keeps 16 parts' loads (16 bytes each) in flight at once.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -21,37 +21,42 @@ namespace {
 
 constexpr int D = kHeadDim;
 
+typedef float floatx4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
 template <typename T>
-__device__ __forceinline__ void store_out(T* o, size_t i, float v);
+__device__ __forceinline__ void store_out(T* o, size_t i, floatx4 v);
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t* o, size_t i, float v) {
-  const __bf16 b = static_cast<__bf16>(v);
-  o[i] = __builtin_bit_cast(uint16_t, b);
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* o, size_t i, floatx4 v) {
+  *reinterpret_cast<bf16x4*>(o + i) = __builtin_convertvector(v, bf16x4);
 }
 template <>
-__device__ __forceinline__ void store_out<float>(float* o, size_t i, float v) {
-  o[i] = v;
+__device__ __forceinline__ void store_out<float>(float* o, size_t i, floatx4 v) {
+  *reinterpret_cast<floatx4*>(o + i) = v;
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(int parts, int rows_heads, const float* __restrict__ po,
                                                          const float* __restrict__ plse, T* __restrict__ o,
                                                          float* __restrict__ lse) {
-  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int d = threadIdx.x & 63;
+  const int rh = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int d4 = (threadIdx.x & 15) * 4;
   if (rh >= rows_heads) return;
-  // Parts are consumed in batches of 8 whose loads are all issued together;
+  // Parts are consumed in batches of 16 whose loads are all issued together;
   // the running maximum m keeps the weights finite across batches.
-  constexpr int B = 8;
-  float m = -INFINITY, z = 0.f, acc = 0.f;
+  constexpr int B = 16;
+  float m = -INFINITY, z = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int i0 = 0; i0 < parts; i0 += B) {
-    float li[B], oi[B];
+    float li[B];
+    floatx4 oi[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int i = i0 + j;
       const bool ok = i < parts;
       li[j] = ok ? plse[static_cast<size_t>(i) * rows_heads + rh] : -INFINITY;
-      oi[j] = ok ? po[(static_cast<size_t>(i) * rows_heads + rh) * D + d] : 0.f;
+      oi[j] = ok ? *reinterpret_cast<const floatx4*>(po + (static_cast<size_t>(i) * rows_heads + rh) * D + d4)
+                 : floatx4{0.f, 0.f, 0.f, 0.f};
     }
     float mb = li[0];
 #pragma unroll
@@ -67,12 +72,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int parts, int rows_hea
     for (int j = 0; j < B; ++j) {
       const float w = li[j] == -INFINITY ? 0.f : __expf(li[j] - m);
       z += w;
-      acc = __builtin_fmaf(w, oi[j], acc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(w, oi[j][k], acc[k]);
     }
   }
-  const float out = z > 0.f ? acc / z : 0.f;
-  store_out<T>(o, static_cast<size_t>(rh) * D + d, out);
-  if (lse && d == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
+  floatx4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = z > 0.f ? acc[k] / z : 0.f;
+  store_out<T>(o, static_cast<size_t>(rh) * D + d4, out);
+  if (lse && d4 == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
 }  // namespace
@@ -81,7 +89,7 @@ hipError_t launch_attn_merge(int dtype, int num_parts, int rows, int num_heads, 
                              const float* part_lse, void* o, float* lse, hipStream_t stream) {
   const int rh = rows * num_heads;
   if (rh == 0) return hipSuccess;
-  const dim3 grid((rh + 3) / 4);
+  const dim3 grid((rh + 15) / 16);
   if (dtype == 0)
     hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, grid, dim3(256), 0, stream, num_parts, rh, part_o, part_lse,
                        static_cast<uint16_t*>(o), lse);

@@ -123,7 +123,7 @@ def test_chunked_full_size_sampled_rows():
     gk, gv = oc.gather()
     assert gk.shape[1] == 43968
     rng = np.random.default_rng(3)
-    rows = np.sort(np.concatenate([rng.choice(tokens, 60, replace=False), [0, 255, 256, 271, 272, 287, 288, 543, 544, tokens - 1]]))
+    rows = np.sort(np.concatenate([rng.choice(tokens, 60, replace=False), [0, 255, 256, 271, 272, 287, 288, 511, 512, 543, 544, tokens - 1]]))
     rows = np.unique(rows)
     _sampled_rows(o, lse, q[rows], torch.from_numpy(rows).cuda(), bits_f64(gk), bits_f64(gv), "chunk rows")
 
@@ -149,7 +149,7 @@ def test_global_and_frame_attention_full_size_sampled_rows():
     k_all = bits_f64(np.concatenate(ks)).transpose(1, 0, 2)
     v_all = bits_f64(np.concatenate(vs)).transpose(1, 0, 2)
     rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([rng.choice(F * T, 40, replace=False), [0, 271, 272, 287, 288, 543, 544, F * T - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(F * T, 40, replace=False), [0, 255, 256, 271, 272, 287, 288, 511, 512, 543, 544, F * T - 1]]))
     _sampled_rows(o, lse, qall[rows], torch.from_numpy(rows).cuda(), k_all, v_all, "global rows")
     # per-frame attention: 100 sequences, each against its own 6 pages (last one 94 tokens)
     ids, lens = dc.visible_table()
