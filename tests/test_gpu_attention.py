@@ -167,6 +167,52 @@ def test_query_counts_across_tile_shapes(qn):
         check_attention(o, lse, ro, rl, "bf16", f"q={qn} splits={splits} Lk={gk.shape[1]}")
 
 
+@pytest.mark.parametrize("qn", [262, 256])
+def test_late_keys_outgrow_running_maximum(qn):
+    """Scores of later pages exceed every earlier one by far more than 16 log2
+    units, so the kernel's rescale path (tile maximum taken again, O and row sum
+    rescaled) runs, on the 32-row blocks and on the 16-row extra block (262
+    queries); partial first pages exercise the first-tile maximum with masked
+    keys."""
+    import torch
+    from paged_sliding_window_kv_amd import paged_attention
+    log(f"late large scores q={qn}")
+    rng = np.random.default_rng(77)
+    H, P, N = 2, 256, 16
+    ids = rng.choice(N, size=6, replace=False).astype(np.int32)
+    lens = np.array([37, 256, 130, 256, 256, 200], np.int32)
+    kv = np.array([0, 6], np.int32)
+    qo = np.array([0, qn], np.int32)
+    kpool = synth.normal_tokens(9, 0, qn, 1, N * H * P, 1, 64, "f32").reshape(N, H, P, 64)
+    vpool = synth.normal_tokens(9, 0, qn, 2, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    q = synth.normal_tokens(9, 0, qn, 0, qn, H, 64, "f32")
+    # every query shares a component along a unit direction u (per head), and the
+    # keys of the last three pages are long along u: their scores exceed the
+    # first pages' by tens of natural-log units
+    u = rng.standard_normal((H, 64))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    q = (q + 4.0 * u[None]).astype(np.float32)
+    for j, p_ in enumerate(ids[3:]):
+        kpool[p_] += ((30.0 + 6 * j) * u[:, None, :]).astype(np.float32)
+    kb = synth.f32_to_bf16_bits(kpool)
+    qb = synth.f32_to_bf16_bits(q)
+    kd = to_dev(kb, "bf16")
+    vd = to_dev(v_pool_device_layout(vpool), "bf16")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    gk = np.concatenate([kb[p_, :, :n] for p_, n in zip(ids, lens)], axis=1)
+    gv = np.concatenate([vpool[p_, :, :n] for p_, n in zip(ids, lens)], axis=1)
+    ro, rl = attention_f64(bits_f64(qb), bits_f64(gk), bits_f64(gv))
+    # the late keys dominate: for most rows the maximum exceeds the first page's by
+    # more than 12 (natural log), i.e. more than 16 log2 units
+    s = np.einsum("qhd,hkd->hqk", bits_f64(qb), bits_f64(gk)) / 8.0
+    gap = s.max(axis=-1) - s[:, :, :37].max(axis=-1)
+    assert (gap > 12.0).mean() > 0.75
+    for splits in (1, 2):
+        o, lse = paged_attention(to_dev(qb, "bf16"), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
+                                 max_qo_len=qn, max_kv_pages=6, num_splits=splits)
+        check_attention(o, lse, ro, rl, "bf16", f"q={qn} splits={splits}")
+
+
 def test_page_order_and_placement_invariance():
     import torch
     from paged_sliding_window_kv_amd import paged_attention
