@@ -493,7 +493,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
       const uint16_t* lk = odd ? lkb : lka;
       const uint16_t* lv = odd ? lvb : lva;
       // Scores of the tile (keys 0..31 then 32..63, four K fragments live at
-      // a time), keys past nk set to -inf.
+      // a time: four reads, then their four products), keys past nk set to
+      // -inf.
       auto scores = [&](floatx16& s0, floatx16& s1) {
         bf16x8 qf[4];
 #pragma unroll
@@ -507,6 +508,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
           for (int st = 0; st < 4; ++st) kf[st] = lds_frag(lk, lr, 2 * st + lh);
 #pragma unroll
           for (int st = 0; st < 4; ++st) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s0, 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x8, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         {
@@ -515,6 +518,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
           for (int st = 0; st < 4; ++st) kf[st] = lds_frag(lk, 32 + lr, 2 * st + lh);
 #pragma unroll
           for (int st = 0; st < 4; ++st) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s1, 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x8, 4, 0);
         }
         __builtin_amdgcn_s_setprio(0);
         if (nk < KT) {
@@ -563,18 +568,28 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
       l_run += lt;
       // V fragments are read only now: reading them during the softmax would
       // keep K, V and the scores live together (other waves hide the wait).
+      // Each half of O^T takes four reads, then its four products.
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 va[4], vb[4];
+      bf16x8 pb[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        va[t] = lds_frag(lv, lr, 2 * t + lh);
-        vb[t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+      for (int t = 0; t < 4; ++t) pb[t] = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
+      {
+        bf16x8 vf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vf[t] = lds_frag(lv, lr, 2 * t + lh);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pb[t], o0, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x8, 4, 0);
       }
+      {
+        bf16x8 vf[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 pb = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[t], pb, o1, 0, 0, 0);
+        for (int t = 0; t < 4; ++t) vf[t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pb[t], o1, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x8, 4, 0);
       }
     }
 

@@ -23,7 +23,13 @@ namespace kvc {
 namespace {
 
 constexpr int kTile = 64;
-constexpr int kThreads = 256;
+// One thread per 16-byte chunk of a tile's K rows (and of its V rows), so each
+// thread issues its loads once and no thread loops over memory round trips:
+// 512 threads for bf16, 1024 for fp32.
+template <typename T>
+constexpr int append_threads() {
+  return kTile * (kHeadDim * static_cast<int>(sizeof(T)) / 16);
+}
 
 struct Dest {
   int32_t page;
@@ -39,7 +45,8 @@ __device__ __forceinline__ Dest dest_of(const AppendParams& p, int tok) {
 
 // T: element type (uint16_t bf16 pattern or float).  VEC elements per 16 bytes.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void kv_append_kernel(const AppendParams p) {
+__global__ __launch_bounds__(append_threads<T>()) void kv_append_kernel(const AppendParams p) {
+  constexpr int kThreads = append_threads<T>();
   constexpr int VEC = 16 / sizeof(T);
   constexpr int D = kHeadDim;
   constexpr int CHUNKS = D / VEC;  // 16-byte chunks per token row
@@ -143,8 +150,10 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
 }
 
 constexpr int kFp8RowThreads = 8;  // threads per (token, head) row, 8 values each
+constexpr int kFp8Threads = 2 * kTile * kFp8RowThreads;  // every K and V row of a tile at once
 
-__global__ __launch_bounds__(kThreads) void kv_append_fp8_kernel(const AppendParams p) {
+__global__ __launch_bounds__(kFp8Threads) void kv_append_fp8_kernel(const AppendParams p) {
+  constexpr int kThreads = kFp8Threads;
   constexpr int D = kHeadDim;
   const int h = blockIdx.y;
   const int H = p.num_heads;
@@ -204,11 +213,11 @@ hipError_t launch_kv_append(const AppendParams& p, int dtype, hipStream_t stream
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, p.num_heads);
   if (dtype == 0)
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(append_threads<uint16_t>()), 0, stream, p);
   else if (dtype == 1)
-    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(append_threads<float>()), 0, stream, p);
   else
-    hipLaunchKernelGGL(kv_append_fp8_kernel, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kv_append_fp8_kernel, grid, dim3(kFp8Threads), 0, stream, p);
   return hipGetLastError();
 }
 
