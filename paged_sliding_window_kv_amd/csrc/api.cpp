@@ -294,6 +294,10 @@ int setup_attn(const paged_attn_args& a, kvc::AttnParams& p, int* splits_out) {
     p.part_o = static_cast<float*>(a.workspace);
     const size_t obytes = (static_cast<size_t>(splits) * rh * kvc::kHeadDim * sizeof(float) + 255) & ~size_t(255);
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + obytes);
+    // The fp16 form of the bf16/FP8 kernels uses the first half of the O
+    // region for the values and the second half for the scales.
+    p.part_o16 = static_cast<_Float16*>(a.workspace);
+    p.part_scale = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + obytes / 2);
   }
   p.qo_indptr = a.qo_indptr;
   p.kv_indptr = a.kv_indptr;
@@ -322,9 +326,12 @@ int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_
                                                  : kvc::launch_attn_f32(src, st);
   if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
   if (splits > 1) {
-    // o is bf16 for FP8 caches
-    const int odt = a.dtype == KVC_DTYPE_F32 ? KVC_DTYPE_F32 : KVC_DTYPE_BF16;
-    e = kvc::launch_attn_merge(odt, splits, a.total_q, a.num_heads, p.part_o, p.part_lse, a.o, a.lse, st);
+    // fp32 caches: fp32 partials; bf16 and FP8 caches: fp16 partials, o bf16
+    e = a.dtype == KVC_DTYPE_F32
+            ? kvc::launch_attn_merge(KVC_DTYPE_F32, splits, a.total_q, a.num_heads, p.part_o, p.part_lse, a.o,
+                                     a.lse, st)
+            : kvc::launch_attn_merge16(splits, a.total_q, a.num_heads, p.part_o16, p.part_scale, p.part_lse, a.o,
+                                       a.lse, st);
     if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   }
   return KVC_OK;

@@ -70,6 +70,7 @@ typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float floatx8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef float floatx4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef _Float16 halfx4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -279,8 +280,6 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
   const int blk = odd ? wave - NB : wave;
   const int wrow0 = row0 + blk * 32;
   const bool active = wrow0 < qn;
-  const int qrow = wrow0 + lr;
-  const bool qvalid = qrow < qn;
   // Extra block (XB): 16 rows NB*32 .. NB*32+15 of the tile, on 16x16x32
   // products; waves 0..3 each take one 32-key quarter of every 128-key step.
   const int xrow0 = row0 + NB * 32;
@@ -683,10 +682,15 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
 
   // ---- epilogue ---------------------------------------------------------------
   // Writes one row's result: normalised O (bf16) and lse, or the split's
-  // partial O (fp32) and lse.  `get(j)` returns the unnormalised O of dims
+  // partial O and lse.  `get(j)` returns the unnormalised O of dims
   // d0[j/4] + j%4 (4 dims per run, `runs` runs); m is the maximum, ltot the
-  // row sum; the lse is written by lanes with `lse_lane`.
-  auto write_row = [&](int row, auto get, const int* d0, auto runs_c, float m, float ltot, bool lse_lane) {
+  // row sum; the lse is written by lanes with `lse_lane`.  A partial O goes
+  // out in fp16 as O * 2^-E, E the smallest non-negative integer that keeps
+  // the row's largest magnitude within 2^15 (0 for any ordinary row), with
+  // 2^E beside it; `row_max` combines a lane's maximum with those of the
+  // other lanes holding the same row (which share the row's validity).
+  auto write_row = [&](int row, auto get, const int* d0, auto runs_c, float m, float ltot, bool lse_lane,
+                       auto row_max) {
     constexpr int runs = decltype(runs_c)::value;
     const bool empty = !(ltot > 0.f);
     const float inv = empty ? 0.f : 1.f / ltot;
@@ -703,15 +707,30 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
       }
       if (p.lse && lse_lane) p.lse[orow] = lse_nat;
     } else {
-      float* po = p.part_o + (static_cast<size_t>(split) * p.total_q * H + orow) * D;
+      const size_t prow = static_cast<size_t>(split) * p.total_q * H + orow;
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4 * runs; ++j) amax = fmaxf(amax, fabsf(get(j) * inv));
+      amax = row_max(amax);
+      int e2 = 0;
+      if (amax > 32768.f) {
+        int fe;
+        frexpf(amax, &fe);  // amax <= 2^fe
+        e2 = fe - 15;
+      }
+      const float down = __builtin_ldexpf(inv, -e2);
+      _Float16* po = p.part_o16 + prow * D;
 #pragma unroll
       for (int r4 = 0; r4 < runs; ++r4) {
         floatx4 f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f[j] = get(r4 * 4 + j) * inv;
-        *reinterpret_cast<floatx4*>(po + d0[r4]) = f;
+        for (int j = 0; j < 4; ++j) f[j] = get(r4 * 4 + j) * down;
+        *reinterpret_cast<halfx4*>(po + d0[r4]) = __builtin_convertvector(f, halfx4);
       }
-      if (lse_lane) p.part_lse[static_cast<size_t>(split) * p.total_q * H + orow] = lse_nat;
+      if (lse_lane) {
+        p.part_lse[prow] = lse_nat;
+        p.part_scale[prow] = __builtin_ldexpf(1.f, e2);
+      }
     }
   };
 
@@ -775,7 +794,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
       if (qvalid) {
         // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
         const int d0[8] = {4 * lh, 8 + 4 * lh, 16 + 4 * lh, 24 + 4 * lh, 32 + 4 * lh, 40 + 4 * lh, 48 + 4 * lh, 56 + 4 * lh};
-        write_row(qrow, [&](int j) { return j < 16 ? o0[j] : o1[j - 16]; }, d0, std::integral_constant<int, 8>{}, M, l_tot, lh == 0);
+        write_row(qrow, [&](int j) { return j < 16 ? o0[j] : o1[j - 16]; }, d0, std::integral_constant<int, 8>{}, M, l_tot, lh == 0,
+                [](float x) { return pair_max(x); });
       }
     }
     if (XB && xactive && wave == 0) {
@@ -809,7 +829,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
       if (xrow < qn) {
         // 16x16 accumulator: element i of xo[db] is dim 16*db + 4*g4 + i.
         const int d0[4] = {4 * g4, 16 + 4 * g4, 32 + 4 * g4, 48 + 4 * g4};
-        write_row(xrow, [&](int j) { return xo[j >> 2][j & 3]; }, d0, std::integral_constant<int, 4>{}, M, l_tot, g4 == 0);
+        write_row(xrow, [&](int j) { return xo[j >> 2][j & 3]; }, d0, std::integral_constant<int, 4>{}, M, l_tot, g4 == 0,
+                  [](float x) { return quad_max(x); });
       }
     }
   }

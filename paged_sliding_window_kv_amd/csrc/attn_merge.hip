@@ -23,6 +23,7 @@ constexpr int D = kHeadDim;
 
 typedef float floatx4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef _Float16 halfx4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* o, size_t i, floatx4 v);
@@ -83,6 +84,58 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int parts, int rows_hea
   if (lse && d4 == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
+// The same merge over partials in the fp16 form of the bf16 and FP8 attention
+// kernels: part i holds O_i * 2^-E_i in fp16 and 2^E_i in part_scale, so its
+// term is exp(lse_i - lse) * 2^E_i * (stored values).  Output bf16.
+__global__ __launch_bounds__(256) void attn_merge16_kernel(int parts, int rows_heads, const _Float16* __restrict__ po,
+                                                           const float* __restrict__ pscale,
+                                                           const float* __restrict__ plse, uint16_t* __restrict__ o,
+                                                           float* __restrict__ lse) {
+  const int rh = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int d4 = (threadIdx.x & 15) * 4;
+  if (rh >= rows_heads) return;
+  constexpr int B = 16;
+  float m = -INFINITY, z = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < parts; i0 += B) {
+    float li[B], si[B];
+    halfx4 oi[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = i0 + j;
+      const bool ok = i < parts;
+      const size_t r = static_cast<size_t>(i) * rows_heads + rh;
+      li[j] = ok ? plse[r] : -INFINITY;
+      si[j] = ok ? pscale[r] : 0.f;
+      oi[j] = ok ? *reinterpret_cast<const halfx4*>(po + r * D + d4) : halfx4{};
+    }
+    float mb = li[0];
+#pragma unroll
+    for (int j = 1; j < B; ++j) mb = fmaxf(mb, li[j]);
+    if (mb == -INFINITY) continue;
+    if (mb > m) {
+      const float c = m == -INFINITY ? 0.f : __expf(m - mb);
+      z *= c;
+      acc *= c;
+      m = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const float w = li[j] == -INFINITY ? 0.f : __expf(li[j] - m);
+      z += w;
+      const float ws = w * si[j];
+      const floatx4 f = __builtin_convertvector(oi[j], floatx4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(ws, f[k], acc[k]);
+    }
+  }
+  floatx4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = z > 0.f ? acc[k] / z : 0.f;
+  store_out<uint16_t>(o, static_cast<size_t>(rh) * D + d4, out);
+  if (lse && d4 == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_attn_merge(int dtype, int num_parts, int rows, int num_heads, const float* part_o,
@@ -96,6 +149,17 @@ hipError_t launch_attn_merge(int dtype, int num_parts, int rows, int num_heads, 
   else
     hipLaunchKernelGGL(attn_merge_kernel<float>, grid, dim3(256), 0, stream, num_parts, rh, part_o, part_lse,
                        static_cast<float*>(o), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge16(int num_parts, int rows, int num_heads, const _Float16* part_o16,
+                               const float* part_scale, const float* part_lse, void* o, float* lse,
+                               hipStream_t stream) {
+  const int rh = rows * num_heads;
+  if (rh == 0) return hipSuccess;
+  const dim3 grid((rh + 15) / 16);
+  hipLaunchKernelGGL(attn_merge16_kernel, grid, dim3(256), 0, stream, num_parts, rh, part_o16, part_scale, part_lse,
+                     static_cast<uint16_t*>(o), lse);
   return hipGetLastError();
 }
 

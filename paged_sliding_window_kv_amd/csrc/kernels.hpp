@@ -50,8 +50,12 @@ struct AttnParams {
   const void* v_pool;
   void* o;                // [total_q][H][d]
   float* lse;             // [total_q][H] or null
-  float* part_o;          // [splits][total_q][H][d] when splits > 1
+  float* part_o;          // [splits][total_q][H][d] when splits > 1 (fp32 kernel)
   float* part_lse;        // [splits][total_q][H]
+  // bf16/FP8 kernels: partial O in fp16 as O * 2^-E (E >= 0, so that every
+  // value stays within fp16 range), with 2^E per (split, row, head).
+  _Float16* part_o16;     // [splits][total_q][H][d]
+  float* part_scale;      // [splits][total_q][H]
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
   const int32_t* page_ids;
@@ -140,5 +144,9 @@ hipError_t launch_attn_f32(const AttnParamsInline& p, hipStream_t stream);
 
 hipError_t launch_attn_merge(int dtype, int num_parts, int rows, int num_heads, const float* part_o,
                              const float* part_lse, void* o, float* lse, hipStream_t stream);
+// Partials in the fp16 form (part_o16, part_scale); o is bf16.
+hipError_t launch_attn_merge16(int num_parts, int rows, int num_heads, const _Float16* part_o16,
+                               const float* part_scale, const float* part_lse, void* o, float* lse,
+                               hipStream_t stream);
 
 }  // namespace kvc

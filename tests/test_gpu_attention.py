@@ -213,6 +213,34 @@ def test_late_keys_outgrow_running_maximum(qn):
         check_attention(o, lse, ro, rl, "bf16", f"q={qn} splits={splits}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_split_partials_with_values_beyond_fp16_range(dtype):
+    """V scaled by 2^20 (exact in bf16): the split partials, kept in fp16 with a
+    per-row power-of-two scale, must not overflow; O / 2^20 matches the oracle's.
+    262 queries (32-row blocks and the 16-row extra block), forced key splits."""
+    import torch
+    from paged_sliding_window_kv_amd import KvCache
+    log(f"values beyond fp16 range, {dtype}")
+    H, P, X, S, W, frames = 2, 256, 6, 1, 2, 5
+    dc = KvCache(num_heads=H, dtype=dtype, patch_tokens=P, special_tokens=X, num_scale_units=S, window_units=W,
+                 max_units=frames, device="cuda")
+    oc = _oracle(dtype, H, P, X, S, W, frames)
+    big = 2.0 ** 20
+    for t in range(frames):
+        q, k, v = synth.frame_qkv(31, 0, t, P + X, H, 64, "bf16")
+        vb = synth.f32_to_bf16_bits((synth.bf16_bits_to_f32(v) * np.float32(big)).astype(np.float32))
+        oc.append(k, vb)
+        dc.append(to_dev(k, "bf16"), to_dev(vb, "bf16"))
+    for splits in (2, 3):
+        o, lse = dc.attend(to_dev(q, "bf16"), num_splits=splits)
+        gk, gv = oc.gather()
+        ro, rl = attention_f64(bits_f64(q), bits_f64(gk), bits_f64(gv))
+        assert np.abs(ro).max() > 32768.0 * 4
+        got = to_f64(o)
+        assert np.isfinite(got).all()
+        check_attention(torch.from_numpy(got / big), lse, ro / big, rl, "bf16", f"{dtype} splits={splits}")
+
+
 def test_page_order_and_placement_invariance():
     import torch
     from paged_sliding_window_kv_amd import paged_attention
