@@ -69,20 +69,54 @@ int rows_per_tile(const paged_attn_args& a) {
   return a.dtype != KVC_DTYPE_F32 ? kvc::attn_bf16_rows_per_tile(choose_waves(a)) : kvc::attn_f32_rows_per_tile();
 }
 
+// Workgroups the chip holds at once: one bf16/FP8 workgroup per compute unit
+// (each uses more than half of a unit's LDS), several one-wave fp32 ones.
+long workgroup_slots(const paged_attn_args& a) { return a.dtype != KVC_DTYPE_F32 ? 256 : 512; }
+
+long query_tiles(const paged_attn_args& a) {
+  const int rows = rows_per_tile(a);
+  return static_cast<long>((a.max_qo_len + rows - 1) / rows) * a.num_seqs * a.num_heads;
+}
+
+// Key splits for tables of up to `pages` pages per sequence.  Query tiles that
+// already fill the chip are not split.  Otherwise the split count s (at most
+// 64, and at least two pages per split so the merge traffic stays small
+// against the K/V reads) minimises the modelled time: rounds of workgroups,
+// ceil(tiles * s / slots), times the work of one workgroup, pages / s plus a
+// fixed 3/4 page (prologue, first loads, epilogue).  A LingBot frame's 16 tiles
+// get 16 splits (one round); 6 batched streams' 96 tiles get 8 (three full
+// rounds) rather than 3 (a full round and a nearly empty one).
+int splits_for_pages(const paged_attn_args& a, long tiles, int pages) {
+  const long slots = workgroup_slots(a);
+  if (pages <= 1 || tiles >= slots) return 1;
+  const int smax = std::max(1, std::min(64, pages / 2));
+  double best = 0.0;
+  int bs = 1;
+  for (int s = 1; s <= smax; ++s) {
+    const long rounds = (tiles * s + slots - 1) / slots;
+    const double cost = static_cast<double>(rounds) * (static_cast<double>(pages) / s + 0.75);
+    if (s == 1 || cost < best * (1.0 - 1e-9)) {
+      best = cost;
+      bs = s;
+    }
+  }
+  return bs;
+}
+
 int choose_splits(const paged_attn_args& a) {
   if (a.num_splits > 0) return std::max(1, std::min(a.num_splits, std::max(1, a.max_kv_pages)));
-  if (a.max_kv_pages <= 1) return 1;
-  const int rows = rows_per_tile(a);
-  const long tiles = static_cast<long>((a.max_qo_len + rows - 1) / rows) * a.num_seqs * a.num_heads;
-  // Aim for about one round of workgroups over the 256 compute units (two per
-  // unit for narrow workgroups), keeping at least two pages per split so the
-  // merge traffic stays small against the K/V reads.
-  const int waves = a.dtype != KVC_DTYPE_F32 ? choose_waves(a) : 1;
-  const long target = waves <= 4 ? 512 : 256;
-  if (tiles >= target) return 1;
-  long s = (target + tiles - 1) / tiles;
-  s = std::min<long>(s, std::max(1, a.max_kv_pages / 2));
-  return static_cast<int>(std::max<long>(1, std::min<long>(s, 64)));
+  return splits_for_pages(a, query_tiles(a), a.max_kv_pages);
+}
+
+// The largest split count any call with up to a.max_kv_pages pages per
+// sequence (and otherwise these arguments) can get: workspace sizes use it, so
+// a workspace sized for a cache's largest table serves every smaller one.
+int max_splits(const paged_attn_args& a) {
+  if (a.num_splits > 0) return choose_splits(a);
+  const long tiles = query_tiles(a);
+  int m = 1;
+  for (int w = 1; w <= a.max_kv_pages; ++w) m = std::max(m, splits_for_pages(a, tiles, w));
+  return m;
 }
 
 int check_attn_args(const paged_attn_args* a) {
@@ -256,7 +290,7 @@ int kvc_get_state(const kvc_t* c, kvc_state* st) {
 int paged_attn_workspace_size(const paged_attn_args* a, size_t* bytes) {
   if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
   if (int s = check_attn_args(a)) return s;
-  *bytes = workspace_for(*a, choose_splits(*a));
+  *bytes = workspace_for(*a, max_splits(*a));
   return KVC_OK;
 }
 
@@ -410,7 +444,7 @@ int kvc_attend_workspace_size(const kvc_t* c, int32_t num_q, size_t* bytes) {
   const int32_t max_entries = std::min<int32_t>(c->pc.num_pages(), kvc::kMaxInlinePages);
   const paged_attn_args a = cache_attn_args(c, num_q, max_entries, 0.f);
   if (int s = check_attn_args(&a)) return s;
-  *bytes = workspace_for(a, choose_splits(a));
+  *bytes = workspace_for(a, max_splits(a));
   return KVC_OK;
 }
 
@@ -547,7 +581,7 @@ int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_cach
   int32_t off[kvc::kMaxInlineSeqs];
   if (int s = batch_args(caches, num_caches, qo_indptr, 0.f, &a, off)) return s;
   if (int s = check_attn_args(&a)) return s;
-  *bytes = workspace_for(a, choose_splits(a));
+  *bytes = workspace_for(a, max_splits(a));
   return KVC_OK;
 }
 
