@@ -110,6 +110,21 @@ __device__ __forceinline__ bf16x8 to_bf16x8(floatx16 s, int base) {
   return __builtin_convertvector(f, bf16x8);
 }
 
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float floatx2 __attribute__((__vector_size__(2 * sizeof(float))));
+
+// One v_cvt_pk_bf16_f32 (round to nearest even); cat4 assembles four pairs
+// into one operand fragment (element 2q+i of the result is element i of pair q).
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) {
+  const floatx2 f = {a, b};
+  return __builtin_convertvector(f, bf16x2);
+}
+__device__ __forceinline__ bf16x8 cat4(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Lanes l and l+32 hold the two halves of a query's keys; these combine the
 // pair with one v_permlane32_swap (which hands each lane its partner's value)
 // instead of an LDS permute.  With operands (x, y) the instruction returns
@@ -836,6 +851,427 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256-row tiles: software-pipelined kernel.
+//
+// On CDNA4 a wave's vector (VALU) work overlaps matrix products well only when
+// the same wave issues them interleaved: products that other waves queue on a
+// busy matrix core hold the issue port, so the attn_bf16_kernel layout (each
+// wave: all products of a tile, then its softmax, then the next products)
+// runs products and softmax one after the other.  Here eight waves (two per
+// SIMD, up to 256 registers each) each own 32 query rows of the tile over
+// every key tile, with their queries in registers, and interleave their own
+// instruction streams:
+//  * block 1 of iteration j: the 8 products of tile j+1's scores, issued
+//    between the exponentials, bf16 conversion and row sums of the second
+//    half (keys 32..63) of tile j;
+//  * block 2: the 8 P V products of tile j, issued between the exponentials
+//    and conversion of the first half (keys 0..31) of tile j+1.
+// Numerics are the attn_bf16_kernel's: S^T = K Q^T on 32x32x16 products,
+// probabilities against the running maximum accepted when every lane's sum
+// is at most kSumBound (else the tile's scores are formed again from LDS,
+// O and the sums rescaled to the tile maximum), P rounded to bf16, fp32
+// accumulators, the same partial-output format for key splits.  The K/V ring,
+// its direct loads, the swizzle, the V pool slot order and the masking of
+// keys past a page's length are shared with the attn_bf16_kernel.
+template <class Src>
+__global__ __launch_bounds__(512) void attn_pipe_kernel(const Src src) {
+  constexpr int W = 8;                   // waves, one per 32-row block
+  constexpr int ROWS = W * 32;
+  constexpr int LPT = DMA_PER_TILE / W;  // direct loads per wave per tile
+  constexpr int SMEM = STAGES * 2 * TILE_ELEMS * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  uint16_t* const lds_t = reinterpret_cast<uint16_t*>(smem);
+  const AttnParams& p = attn_base(src);
+
+  // ---- which (sequence, head, split, query tile): as attn_bf16_kernel -----
+  const int L = blockIdx.x;
+  const int g = L % p.groups_padded;
+  const int qt = L / p.groups_padded;
+  if (g >= p.groups) return;
+  const int split = g % p.num_splits;
+  const int sh = g / p.num_splits;
+  const int h = sh % p.num_heads;
+  const int seq = sh / p.num_heads;
+  int q0, qn, ebase, ecount;
+  attn_seq(src, seq, q0, qn, ebase, ecount);
+  const int row0 = qt * ROWS;
+  if (row0 >= qn) return;
+  const int per = (ecount + p.num_splits - 1) / p.num_splits;
+  const int eb = ebase + min(ecount, split * per);
+  const int ee = ebase + min(ecount, (split + 1) * per);
+
+  const int H = p.num_heads;
+  const int P = p.page_size;
+  const float sl2 = p.scale_log2;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int wrow0 = row0 + wave * 32;
+  const bool active = wrow0 < qn;  // wave-uniform; idle waves still load and synchronise
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v_pool);
+  const size_t page_stride = static_cast<size_t>(H) * P * D;
+  const size_t head_off = static_cast<size_t>(h) * P * D;
+
+  // ---- queries -> registers: the B operand of S^T = K Q^T, dims 16st+8lh..+7
+  // of row wrow0+lr (rows past the sequence repeat its last row; their
+  // outputs are never written).
+  bf16x8 qf[4];
+  {
+    const int row = min(wrow0 + lr, qn - 1);
+    const bf16x8* gq = reinterpret_cast<const bf16x8*>(qg + (static_cast<size_t>(q0 + row) * H + h) * D + lh * 8);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qf[st] = gq[2 * st];
+  }
+
+  // ---- this wave's share of each tile's 16 direct loads (as attn_bf16_kernel)
+  int dma_goff[LPT], dma_loff[LPT];
+  bool dma_v[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int inst = wave * LPT + j;
+    const int is_v = inst >> 3, part = inst & 7;
+    const int row = part * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    dma_v[j] = is_v != 0;
+    dma_goff[j] = is_v ? row * P + chunk * 8 : row * D + chunk * 8;
+    dma_loff[j] = is_v * TILE_ELEMS + part * 512;
+  }
+  auto issue = [&](const Cursor& c, int stage) {
+    const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
+    const int koff = c.kt * KT * D, voff = c.kt * KT;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
+      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_t + stage * 2 * TILE_ELEMS + dma_loff[j]), 16, 0, 0);
+    }
+  };
+  // Waits for this wave's loads of all tiles but the last `ahead` issued.
+  auto wait_tiles = [&](int ahead) {
+    if (ahead >= 3)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * LPT));
+    else if (ahead == 2)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LPT));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(LPT));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  };
+  // Zero the V^T slots of keys nk..63 of a staged tile (pool slot order, then
+  // the chunk swizzle), as attn_bf16_kernel.
+  auto zero_tail = [&](uint16_t* lv, int nk) {
+    for (int it = tid; it < D * 16; it += W * 64) {
+      const int row = it >> 4, grp = it & 15;
+      const int k0 = grp * 4;
+      if (k0 + 4 <= nk) continue;
+      const int sg = (grp & ~3) | ((grp & 1) << 1) | ((grp >> 1) & 1);
+      const int pos = sg * 4;
+      uint16_t* rp = lv + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (k0 + e >= nk) rp[e] = 0;
+    }
+  };
+  auto stage_ptr = [&](int t) { return lds_t + (t % STAGES) * 2 * TILE_ELEMS; };
+
+  // Scores of a tile from LDS (no interleave: first tile and the rare path).
+  auto scores = [&](const uint16_t* lk, floatx16& s0, floatx16& s1) {
+    bf16x8 kf[8];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      kf[st] = lds_frag(lk, lr, 2 * st + lh);
+      kf[4 + st] = lds_frag(lk, 32 + lr, 2 * st + lh);
+    }
+    s0 = floatx16{};
+    s1 = floatx16{};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s0, 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[4 + st], qf[st], s1, 0, 0, 0);
+  };
+  // Keys nk..63 of a tile get -inf scores (32x32 layout: element r of s0 is
+  // key (r>>2)*8 + 4lh + (r&3), s1 adds 32).
+  auto mask = [&](floatx16& s0, floatx16& s1, int nk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = (r >> 2) * 8 + lh * 4 + (r & 3);
+      if (key >= nk) s0[r] = -INFINITY;
+      if (key + 32 >= nk) s1[r] = -INFINITY;
+    }
+  };
+
+  float m_run = -INFINITY;  // running maximum of scaled scores (log2 domain), per query
+  float l_run = 0.f;        // this lane's partial row sum
+  floatx16 o0 = {}, o1 = {};
+
+  // Softmax state of a tile between the two iterations that form it: the
+  // probabilities of keys 0..31 (P^T fragments 0 and 1, bf16) with this
+  // lane's sum of them, and the raw scores of keys 32..63.
+  struct TileState {
+    bf16x8 pa0, pa1;
+    float sa;
+    floatx16 sb;
+  };
+  auto first_half = [&](const floatx16& s0, TileState& t) {
+    const float nm = -m_run;
+    floatx16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, nm));
+    t.sa = half_sum(e);
+    t.pa0 = to_bf16x8(e, 0);
+    t.pa1 = to_bf16x8(e, 8);
+  };
+  // The rare path: the tile's scores formed again, its maximum taken, O and
+  // the sum rescaled, and all its probabilities formed against the new maximum.
+  auto rescale_tile = [&](const uint16_t* lk, int nk, TileState& t, bf16x8& pb2, bf16x8& pb3) {
+    floatx16 s0, s1;
+    scores(lk, s0, s1);
+    if (nk < KT) mask(s0, s1, nk);
+    const float mx = pair_max(tile_max(s0, s1)) * sl2;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o0[r] *= alpha;
+      o1[r] *= alpha;
+    }
+    first_half(s0, t);
+    const float nm = -m_run;
+    floatx16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, nm));
+    pb2 = to_bf16x8(e, 0);
+    pb3 = to_bf16x8(e, 8);
+    return t.sa + half_sum(e);
+  };
+  // Second half of a tile's probabilities (keys 32..63) against m_run; returns
+  // this lane's sum over the whole tile.
+  auto second_half = [&](const TileState& t, bf16x8& pb2, bf16x8& pb3) {
+    const float nm = -m_run;
+    floatx16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(t.sb[r], sl2, nm));
+    pb2 = to_bf16x8(e, 0);
+    pb3 = to_bf16x8(e, 8);
+    return t.sa + half_sum(e);
+  };
+
+  // ---- prologue: first tiles in flight, tile 0's scores ---------------------
+  Cursor lc, cc, cn;  // next tile to issue, tile j, tile j+1
+  cursor_first(src, eb, ee, lc);
+  cc = lc;
+  int ni = 0;
+  for (int s = 0; s < STAGES - 1 && lc.e < ee; ++s) {
+    issue(lc, ni % STAGES);
+    cursor_next(src, ee, lc);
+    ++ni;
+  }
+  TileState A, B;
+  int j = 0;
+  if (ni > 0) {
+    wait_tiles(ni - 1);
+    __builtin_amdgcn_s_barrier();
+    int nkc = min(KT, cc.len - cc.kt * KT);
+    if (nkc < KT) zero_tail(stage_ptr(0) + TILE_ELEMS, nkc);
+    if (active) {
+      floatx16 s0, s1;
+      scores(stage_ptr(0), s0, s1);
+      if (nkc < KT) mask(s0, s1, nkc);
+      m_run = pair_max(tile_max(s0, s1)) * sl2;  // exact maximum of the first tile
+      first_half(s0, A);
+      A.sb = s1;
+    }
+    cn = cc;
+    cursor_next(src, ee, cn);
+
+    // One iteration: finish tile j (state `cur`) and its P V products, form
+    // tile j+1's scores into `nxt`.
+    auto body = [&](TileState& cur, TileState& nxt) {
+      wait_tiles(ni - (j + 2));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+      __builtin_amdgcn_s_barrier();
+      const int nkn = min(KT, cn.len - cn.kt * KT);
+      uint16_t* const lkn = stage_ptr(j + 1);
+      if (nkn < KT) zero_tail(lkn + TILE_ELEMS, nkn);  // published by the next barrier
+      if (active) {
+        const uint16_t* lvc = stage_ptr(j) + TILE_ELEMS;
+        const float nm = -m_run;
+        auto ex = [&](float s) { return __builtin_amdgcn_exp2f(__builtin_fmaf(s, sl2, nm)); };
+        // Each block is eight fenced groups: one product, then the exponentials
+        // of one score pair, the bf16 conversion and sum of the previous pair,
+        // and a share of the fragment reads the next block needs.
+        // block 1: tile j+1's scores under tile j's keys 32..63
+        bf16x8 kf[8], vf[8];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          kf[st] = lds_frag(lkn, lr, 2 * st + lh);
+          kf[4 + st] = lds_frag(lkn, 32 + lr, 2 * st + lh);
+        }
+        float e0 = ex(cur.sb[0]), e1 = ex(cur.sb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx16 n0 = {}, n1 = {};
+        bf16x2 c[8];
+        float u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < 4)
+            n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], n0, 0, 0, 0);
+          else
+            n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i - 4], n1, 0, 0, 0);
+          c[i] = cvt2(e0, e1);
+          u[i] = e0 + e1;
+          if (i < 7) {
+            e0 = ex(cur.sb[2 * i + 2]);
+            e1 = ex(cur.sb[2 * i + 3]);
+          }
+          if (i >= 2 && i < 6) {
+            const int t = i - 2;
+            vf[t] = lds_frag(lvc, lr, 2 * t + lh);
+            vf[4 + t] = lds_frag(lvc, 32 + lr, 2 * t + lh);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 pb2 = cat4(c[0], c[1], c[2], c[3]);
+        bf16x8 pb3 = cat4(c[4], c[5], c[6], c[7]);
+        float lt = cur.sa + (((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7])));
+        if (__any(!(lt <= kSumBound))) {
+          // Rare: K of tile j is still staged (its stage is refilled one
+          // iteration later).
+          lt = rescale_tile(stage_ptr(j), min(KT, cc.len - cc.kt * KT), cur, pb2, pb3);
+        }
+        l_run += lt;
+        if (nkn < KT) mask(n0, n1, nkn);
+        // block 2: tile j's P V products under tile j+1's keys 0..31
+        const float nm2 = -m_run;
+        auto ex2 = [&](float s) { return __builtin_amdgcn_exp2f(__builtin_fmaf(s, sl2, nm2)); };
+        __builtin_amdgcn_sched_barrier(0);
+        float f0 = ex2(n0[0]), f1 = ex2(n0[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 pb[4] = {cur.pa0, cur.pa1, pb2, pb3};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (t < 4)
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pb[t], o0, 0, 0, 0);
+          else
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pb[t - 4], o1, 0, 0, 0);
+          c[t] = cvt2(f0, f1);
+          u[t] = f0 + f1;
+          if (t < 7) {
+            f0 = ex2(n0[2 * t + 2]);
+            f1 = ex2(n0[2 * t + 3]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        nxt.pa0 = cat4(c[0], c[1], c[2], c[3]);
+        nxt.pa1 = cat4(c[4], c[5], c[6], c[7]);
+        nxt.sa = ((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7]));
+        nxt.sb = n1;
+      }
+      // Stage (j-1) % STAGES is free (every wave is past iteration j-1).
+      if (lc.e < ee) {
+        issue(lc, ni % STAGES);
+        cursor_next(src, ee, lc);
+        ++ni;
+      }
+      cc = cn;
+      cursor_next(src, ee, cn);
+      ++j;
+    };
+
+    // Two iterations per trip so that the two states swap roles without copies.
+    while (cn.e < ee) {
+      body(A, B);
+      if (cn.e >= ee) {
+        A = B;
+        break;
+      }
+      body(B, A);
+    }
+
+    // ---- last tile: finish its probabilities and its P V products ---------
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    __builtin_amdgcn_s_barrier();  // publishes the last tile's zeroed V slots
+    if (active) {
+      bf16x8 pb2, pb3;
+      float lt = second_half(A, pb2, pb3);
+      if (__any(!(lt <= kSumBound))) lt = rescale_tile(stage_ptr(j), min(KT, cc.len - cc.kt * KT), A, pb2, pb3);
+      l_run += lt;
+      const uint16_t* lvc = stage_ptr(j) + TILE_ELEMS;
+      const bf16x8 pb[4] = {A.pa0, A.pa1, pb2, pb3};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lvc, lr, 2 * t + lh), pb[t], o0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(lvc, 32 + lr, 2 * t + lh), pb[t], o1, 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: each wave owns its rows; same output forms as attn_bf16_kernel
+  if (!active) return;
+  int t_end = tid;
+  asm volatile("" : "+v"(t_end));
+  const int lane2 = t_end & 63;
+  const int lr2 = lane2 & 31, lh2 = lane2 >> 5;
+  const int qrow = wrow0 + lr2;
+  const float ltot = pair_sum(l_run);
+  if (qrow >= qn) return;
+  const bool empty = !(ltot > 0.f);
+  const float inv = empty ? 0.f : 1.f / ltot;
+  const float lse_nat = empty ? -INFINITY : (m_run + __log2f(ltot)) * 0.69314718055994530942f;
+  const size_t orow = static_cast<size_t>(q0 + qrow) * H + h;
+  // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
+  auto get = [&](int jj) { return jj < 16 ? o0[jj] : o1[jj - 16]; };
+  if (p.num_splits == 1) {
+    uint16_t* og = static_cast<uint16_t*>(p.o) + orow * D;
+#pragma unroll
+    for (int r4 = 0; r4 < 8; ++r4) {
+      floatx4 f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) f[jj] = get(r4 * 4 + jj) * inv;
+      *reinterpret_cast<bf16x4*>(og + r4 * 8 + 4 * lh2) = __builtin_convertvector(f, bf16x4);
+    }
+    if (p.lse && lh2 == 0) p.lse[orow] = lse_nat;
+  } else {
+    // Partial O in fp16 as O * 2^-E, E >= 0 the smallest exponent keeping the
+    // row's largest magnitude within 2^15, 2^E beside the lse.
+    const size_t prow = static_cast<size_t>(split) * p.total_q * H + orow;
+    float amax = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) amax = fmaxf(amax, fabsf(get(jj) * inv));
+    amax = pair_max(amax);
+    int e2 = 0;
+    if (amax > 32768.f) {
+      int fe;
+      frexpf(amax, &fe);
+      e2 = fe - 15;
+    }
+    const float down = __builtin_ldexpf(inv, -e2);
+    _Float16* po = p.part_o16 + prow * D;
+#pragma unroll
+    for (int r4 = 0; r4 < 8; ++r4) {
+      floatx4 f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) f[jj] = get(r4 * 4 + jj) * down;
+      *reinterpret_cast<halfx4*>(po + r4 * 8 + 4 * lh2) = __builtin_convertvector(f, halfx4);
+    }
+    if (lh2 == 0) {
+      p.part_lse[prow] = lse_nat;
+      p.part_scale[prow] = __builtin_ldexpf(1.f, e2);
+    }
+  }
+}
+
 }  // namespace
 
 // blocks <= 8: that many 32-row blocks; 9: eight blocks plus the shared 16-row
@@ -858,8 +1294,13 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
     KVC_CASE(5)
     KVC_CASE(6)
     KVC_CASE(7)
-    KVC_CASE(8)
 #undef KVC_CASE
+    case 8:
+      if constexpr (KV8)
+        hipLaunchKernelGGL((attn_bf16_kernel<8, false, Src, KV8>), grid, dim3(8 * 128), 0, stream, src);
+      else
+        hipLaunchKernelGGL((attn_pipe_kernel<Src>), grid, dim3(8 * 64), 0, stream, src);
+      break;
     case 9:
       hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 128), 0, stream, src);
       break;
