@@ -78,29 +78,40 @@ long query_tiles(const paged_attn_args& a) {
   return static_cast<long>((a.max_qo_len + rows - 1) / rows) * a.num_seqs * a.num_heads;
 }
 
-// Key splits for tables of up to `pages` pages per sequence.  Query tiles that
-// already fill the chip are not split.  Otherwise the split count s (at most
-// 64, and at least two pages per split so the merge traffic stays small
-// against the K/V reads) minimises the modelled time: rounds of workgroups,
-// ceil(tiles * s / slots), times the work of one workgroup, pages / s plus a
-// fixed 3/4 page (prologue, first loads, epilogue).  A LingBot frame's 16 tiles
-// get 16 splits (one round); 6 batched streams' 96 tiles get 8 (three full
-// rounds) rather than 3 (a full round and a nearly empty one).
+// Key splits for tables of up to `pages` pages per sequence.  The split count
+// s (at most 64, and at least two pages per split so the merge traffic stays
+// small against the K/V reads) minimises the modelled time: rounds of
+// workgroups, ceil(tiles * s / slots), times the work of one workgroup, pages /
+// s plus a fixed 3/4 page (prologue, first loads, epilogue), plus the split
+// partials' round trip and merge when s > 1 (about 1/320 of a page-round per
+// query tile and split: 70 KB of fp16 partials per 256-row tile written and
+// read back at HBM rate, against one page of a 256-row tile's products).
+// A LingBot frame's 16 tiles get 16 splits (one round); 6 batched streams' 96
+// tiles get 8 (three full rounds) rather than 3 (a full round and a nearly
+// empty one); a 10,992-query chunk's 688 tiles over 172 pages get 4 (eleven
+// rounds, the last nearly full) rather than 1 (three rounds, the last 69% full).
+// A split is taken only when it beats one split by 3% in the model.
 int splits_for_pages(const paged_attn_args& a, long tiles, int pages) {
   const long slots = workgroup_slots(a);
-  if (pages <= 1 || tiles >= slots) return 1;
+  if (pages <= 1) return 1;
   const int smax = std::max(1, std::min(64, pages / 2));
+  auto cost = [&](int s) {
+    const long rounds = (tiles * s + slots - 1) / slots;
+    const double merge = s > 1 ? static_cast<double>(tiles) * s / 320.0 : 0.0;
+    return static_cast<double>(rounds) * (static_cast<double>(pages) / s + 0.75) + merge;
+  };
   double best = 0.0;
   int bs = 1;
-  for (int s = 1; s <= smax; ++s) {
-    const long rounds = (tiles * s + slots - 1) / slots;
-    const double cost = static_cast<double>(rounds) * (static_cast<double>(pages) / s + 0.75);
-    if (s == 1 || cost < best * (1.0 - 1e-9)) {
-      best = cost;
+  for (int s = 2; s <= smax; ++s) {
+    const double c = cost(s);
+    if (bs == 1 || c < best * (1.0 - 1e-9)) {
+      best = c;
       bs = s;
     }
   }
-  return bs;
+  // Split only for a clear modelled gain (3%): the model is coarse, and a
+  // split adds partial traffic that a near tie does not repay.
+  return bs > 1 && best < 0.97 * cost(1) ? bs : 1;
 }
 
 int choose_splits(const paged_attn_args& a) {
