@@ -284,7 +284,7 @@ def run_stream(args) -> dict:
         "roofline": {
             "bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": ach_gbs / PEAK_HBM_GBS, "traffic": None,
-            "kernel": "paged attention call (attn_bf16_kernel + attn_merge_kernel)",
+            "kernel": "paged attention call (attn_bf16_kernel + attn_merge16_kernel)",
             "avg_call_us": avg_us, "calls": n_launch,
             "bytes_per_call_avg": att_b / n_launch,
             "attn_tflops": att_f / att_s / 1e12,
@@ -395,7 +395,7 @@ def run_stream_batched(args) -> dict:
                                f"262 queries/stream/step, {frames} frames, one attention launch per layer and frame",
                    "streams": B, "layers": L, "frames": frames},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                     "traffic": None, "kernel": "batched attention call (attn_bf16_kernel + attn_merge_kernel)",
+                     "traffic": None, "kernel": "batched attention call (attn_bf16_kernel + attn_merge16_kernel)",
                      "avg_call_us": att / n * 1e6, "calls": n, "attn_tflops": flops / att / 1e12},
     }
 
@@ -491,8 +491,10 @@ def run_chunked(args) -> dict:
                    "keep_ratio": kr, "attended_tokens": lk},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "paged attention call (attn_bf16_kernel)", "avg_call_us": att / n * 1e6,
-                     "calls": n},
+                     "kernel": "paged attention call (attn_pipe_kernel + attn_merge16_kernel)",
+                     "avg_call_us": att / n * 1e6, "calls": n,
+                     "bytes_per_call_avg": sum(attn_bytes(tokens, x, c["heads"]) for x in
+                                               ([lk] * L if kr >= 1.0 else lks)) / L},
     }
 
 
@@ -573,7 +575,7 @@ def run_global(args) -> dict:
                    "layers": L, "heads": H, "head_dim": 64, "tokens": T},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "global attention call (attn_bf16_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
+                     "kernel": "global attention call (attn_pipe_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
                      "frame_attn_tflops": fl_f / tfr / 1e12},
     }
 
@@ -657,6 +659,10 @@ def main():
             res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "chunked":
         res = run_chunked(args)
+        ratio = measured_traffic_ratio("attn_pipe_vggt_chunked.md") if args.keep_ratio >= 1.0 else None
+        if ratio is not None:
+            res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
+            res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "stream_batched":
         res = run_stream_batched(args)
     else:
