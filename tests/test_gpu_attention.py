@@ -167,6 +167,51 @@ def test_query_counts_across_tile_shapes(qn):
         check_attention(o, lse, ro, rl, "bf16", f"q={qn} splits={splits} Lk={gk.shape[1]}")
 
 
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_256_row_tiles_short_and_empty_key_ranges(splits):
+    """256-row query tiles (the 8-wave software-pipelined kernel) against key
+    ranges that leave its pipeline nearly or entirely empty: no keys at all
+    (O = 0, lse = -inf), one token, one page shorter than a 64-key tile, one
+    exactly full tile, and a 5-page range whose forced splits leave whole
+    splits with a single tile; NaN-poisoned stale slots."""
+    import torch
+    from paged_sliding_window_kv_amd import paged_attention
+    log(f"256-row tiles, short key ranges, splits={splits}")
+    rng = np.random.default_rng(55)
+    H, P, N = 2, 256, 16
+    qlens = [300, 257, 512, 300, 270]
+    page_lens = [[], [1], [37], [64], [256, 64, 200, 1, 65]]
+    counts = [len(x) for x in page_lens]
+    ids = rng.choice(N, size=sum(counts), replace=False).astype(np.int32)
+    lens = np.array([n for x in page_lens for n in x], np.int32)
+    kv = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    kpool = synth.normal_tokens(6, 0, 0, 1, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    vpool = synth.normal_tokens(6, 0, 0, 2, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    q = synth.normal_tokens(6, 0, 0, 0, int(qo[-1]), H, 64, "bf16")
+    kd = to_dev(kpool, "bf16")
+    vd = to_dev(v_pool_device_layout(vpool), "bf16")
+    pos = torch.from_numpy(v_positions(P)).cuda()
+    for p_, n in zip(ids, lens):
+        kd[p_, :, n:] = float("nan")
+        vd[p_][:, :, pos[n:]] = float("nan")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    o, lse = paged_attention(to_dev(q, "bf16"), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
+                             max_qo_len=max(qlens), max_kv_pages=max(counts), num_splits=splits)
+    for s_ in range(len(qlens)):
+        a, b = qo[s_], qo[s_ + 1]
+        sel = list(zip(ids[kv[s_]:kv[s_ + 1]], lens[kv[s_]:kv[s_ + 1]]))
+        if sel:
+            gk = np.concatenate([kpool[p_, :, :n] for p_, n in sel], axis=1)
+            gv = np.concatenate([vpool[p_, :, :n] for p_, n in sel], axis=1)
+        else:
+            gk = gv = np.zeros((H, 0, 64), kpool.dtype)
+        ro, rl = attention_f64(bits_f64(q[a:b]), bits_f64(gk), bits_f64(gv))
+        check_attention(o[a:b], lse[a:b], ro, rl, "bf16", f"splits={splits} seq={s_} q={b - a} Lk={gk.shape[1]}")
+        if not sel:
+            assert (to_f64(o[a:b]) == 0).all()
+
+
 @pytest.mark.parametrize("qn", [262, 256])
 def test_late_keys_outgrow_running_maximum(qn):
     """Scores of later pages exceed every earlier one by far more than 16 log2
