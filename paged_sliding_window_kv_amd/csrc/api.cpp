@@ -60,6 +60,7 @@ int choose_waves(const paged_attn_args& a) {
   // per-step work is even across the waves (measured 9% faster on 10,992-row
   // chunks, where the tile counts are 41 and 43).
   const long q = a.max_qo_len;
+  if (a.dtype == KVC_DTYPE_BF16 && q > 1024) return 10;
   if (q <= 256) return std::max(1, static_cast<int>((q + 31) / 32));
   const long t272 = (q + 271) / 272, t256 = (q + 255) / 256;
   return 10 * t256 >= 11 * t272 ? 9 : 8;

@@ -1272,11 +1272,323 @@ __global__ __launch_bounds__(512) void attn_pipe_kernel(const Src src) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 512-row tiles: eight waves, each owning 64 query rows (two 32-row blocks A
+// and B) over every key tile.
+//
+// The 8-wave kernel above is bound by instruction issue, not by the matrix
+// core: per 32x64 unit a wave issues its softmax (about 130 VALU
+// instructions) but also the tile's fragment reads, the table walk and
+// ring bookkeeping (about 69 SALU and 16 LDS instructions), a direct load and
+// a barrier.  Here one wave serves two 32-row blocks with the same K and V
+// fragments, the same table walk and the same barrier, so that work is spent
+// once per 64 rows.  There is no cross-tile pipeline (the two blocks'
+// accumulators take the registers): within a tile, block B's score products
+// are issued between block A's exponentials, and block A's P V products
+// between block B's.  Numerics, ring, masking and output formats are those
+// of the other bf16 kernels.
+template <class Src>
+__global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
+  constexpr int W = 8;                   // waves, one per 64-row pair of blocks
+  constexpr int ROWS = W * 64;
+  constexpr int LPT = DMA_PER_TILE / W;  // direct loads per wave per tile
+  constexpr int SMEM = STAGES * 2 * TILE_ELEMS * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  uint16_t* const lds_t = reinterpret_cast<uint16_t*>(smem);
+  const AttnParams& p = attn_base(src);
+
+  // ---- which (sequence, head, split, query tile): as attn_bf16_kernel -----
+  const int L = blockIdx.x;
+  const int g = L % p.groups_padded;
+  const int qt = L / p.groups_padded;
+  if (g >= p.groups) return;
+  const int split = g % p.num_splits;
+  const int sh = g / p.num_splits;
+  const int h = sh % p.num_heads;
+  const int seq = sh / p.num_heads;
+  int q0, qn, ebase, ecount;
+  attn_seq(src, seq, q0, qn, ebase, ecount);
+  const int row0 = qt * ROWS;
+  if (row0 >= qn) return;
+  const int per = (ecount + p.num_splits - 1) / p.num_splits;
+  const int eb = ebase + min(ecount, split * per);
+  const int ee = ebase + min(ecount, (split + 1) * per);
+
+  const int H = p.num_heads;
+  const int P = p.page_size;
+  const float sl2 = p.scale_log2;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int wrow0 = row0 + wave * 64;  // block A: wrow0..+31, block B: wrow0+32..+63
+  const bool active = wrow0 < qn;      // wave-uniform; idle waves still load and synchronise
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v_pool);
+  const size_t page_stride = static_cast<size_t>(H) * P * D;
+  const size_t head_off = static_cast<size_t>(h) * P * D;
+
+  // ---- queries -> registers (B operands of S^T = K Q^T, dims 16st+8lh..+7);
+  // rows past the sequence repeat its last row, their outputs are never written.
+  bf16x8 qa[4], qb[4];
+  {
+    const int ra = min(wrow0 + lr, qn - 1), rb = min(wrow0 + 32 + lr, qn - 1);
+    const bf16x8* ga = reinterpret_cast<const bf16x8*>(qg + (static_cast<size_t>(q0 + ra) * H + h) * D + lh * 8);
+    const bf16x8* gb = reinterpret_cast<const bf16x8*>(qg + (static_cast<size_t>(q0 + rb) * H + h) * D + lh * 8);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      qa[st] = ga[2 * st];
+      qb[st] = gb[2 * st];
+    }
+  }
+
+  // ---- this wave's share of each tile's 16 direct loads (as attn_bf16_kernel)
+  int dma_goff[LPT], dma_loff[LPT];
+  bool dma_v[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int inst = wave * LPT + j;
+    const int is_v = inst >> 3, part = inst & 7;
+    const int row = part * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    dma_v[j] = is_v != 0;
+    dma_goff[j] = is_v ? row * P + chunk * 8 : row * D + chunk * 8;
+    dma_loff[j] = is_v * TILE_ELEMS + part * 512;
+  }
+  auto issue = [&](const Cursor& c, int stage) {
+    const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
+    const int koff = c.kt * KT * D, voff = c.kt * KT;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
+      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_t + stage * 2 * TILE_ELEMS + dma_loff[j]), 16, 0, 0);
+    }
+  };
+  // Waits for this wave's loads of all tiles but the last `ahead` issued.
+  auto wait_tiles = [&](int ahead) {
+    if (ahead >= 4)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 * LPT));
+    else if (ahead == 3)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * LPT));
+    else if (ahead == 2)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LPT));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(LPT));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  };
+  // Zero the V^T slots of keys nk..63 of a staged tile (as attn_bf16_kernel).
+  auto zero_tail = [&](uint16_t* lv, int nk) {
+    for (int it = tid; it < D * 16; it += W * 64) {
+      const int row = it >> 4, grp = it & 15;
+      const int k0 = grp * 4;
+      if (k0 + 4 <= nk) continue;
+      const int sg = (grp & ~3) | ((grp & 1) << 1) | ((grp >> 1) & 1);
+      const int pos = sg * 4;
+      uint16_t* rp = lv + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (k0 + e >= nk) rp[e] = 0;
+    }
+  };
+  auto stage_ptr = [&](int t) { return lds_t + (t % STAGES) * 2 * TILE_ELEMS; };
+  // Keys nk..63 get -inf scores (32x32 layout: element r of s0 is key
+  // (r>>2)*8 + 4lh + (r&3), s1 adds 32); the lane threshold is formed at each
+  // call so that no per-element key indices stay live across the loop.
+  auto mask = [&](floatx16& s0, floatx16& s1, int nk) {
+    int th = nk - 4 * ((tid >> 5) & 1);
+    asm volatile("" : "+v"(th));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kb = (r >> 2) * 8 + (r & 3);
+      if (kb >= th) s0[r] = -INFINITY;
+      if (kb + 32 >= th) s1[r] = -INFINITY;
+    }
+  };
+  // Scores of one block (queries qv) against the tile's K fragments.
+  auto scores = [&](const bf16x8 (&kf)[8], const bf16x8 (&qv)[4], floatx16& s0, floatx16& s1) {
+    s0 = floatx16{};
+    s1 = floatx16{};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qv[st], s0, 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[4 + st], qv[st], s1, 0, 0, 0);
+  };
+  auto kfrags = [&](const uint16_t* lk, bf16x8 (&kf)[8]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      kf[st] = lds_frag(lk, lr, 2 * st + lh);
+      kf[4 + st] = lds_frag(lk, 32 + lr, 2 * st + lh);
+    }
+  };
+
+  // Per block: running maximum (log2 domain, per query), this lane's partial
+  // row sum, O^T accumulators (dims 0..31 and 32..63).
+  float ma = -INFINITY, mb = -INFINITY, la = 0.f, lb = 0.f;
+  floatx16 oa0 = {}, oa1 = {}, ob0 = {}, ob1 = {};
+
+  // Probabilities of one block against its running maximum m, in place, as
+  // bf16 P^T fragments; returns this lane's sum.  On the block's first tile m
+  // starts at the tile's exact maximum; when a lane's sum exceeds kSumBound
+  // the tile's scores are formed again from LDS, m moves to the tile maximum
+  // and O and the sum are rescaled (as attn_bf16_kernel).
+  auto softmax = [&](floatx16& s0, floatx16& s1, float& m, float& l, floatx16& o0, floatx16& o1,
+                     const uint16_t* lk, const bf16x8 (&qv)[4], int nk, bool first, bf16x8 (&pb)[4]) {
+    if (first) m = pair_max(tile_max(s0, s1)) * sl2;  // every tile holds at least one valid key
+    auto probs = [&]() {
+      const float nm = -m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, nm));
+        s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, nm));
+      }
+      return tile_sum(s0, s1);
+    };
+    float lt = probs();
+    if (__any(!(lt <= kSumBound))) {
+      bf16x8 kf[8];
+      kfrags(lk, kf);
+      scores(kf, qv, s0, s1);
+      if (nk < KT) mask(s0, s1, nk);
+      const float m_new = fmaxf(m, pair_max(tile_max(s0, s1)) * sl2);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o0[r] *= alpha;
+        o1[r] *= alpha;
+      }
+      lt = probs();
+    }
+    l += lt;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pb[t] = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
+  };
+
+  // ---- the key loop: tile j lives in stage j % STAGES ------------------------
+  Cursor lc, cc;
+  cursor_first(src, eb, ee, lc);
+  cc = lc;
+  int ni = 0, j = 0;
+  for (int s = 0; s < STAGES - 1 && lc.e < ee; ++s) {
+    issue(lc, ni % STAGES);
+    cursor_next(src, ee, lc);
+    ++ni;
+  }
+  while (cc.e < ee) {
+    wait_tiles(ni - (j + 1));  // tile j
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    __builtin_amdgcn_s_barrier();
+    // Stage (j-1) % STAGES is free (every wave is past iteration j-1).
+    if (lc.e < ee) {
+      issue(lc, ni % STAGES);
+      cursor_next(src, ee, lc);
+      ++ni;
+    }
+    const int nk = min(KT, cc.len - cc.kt * KT);
+    uint16_t* const lk = stage_ptr(j);
+    if (nk < KT) {  // rare: a page's last, partial tile
+      zero_tail(lk + TILE_ELEMS, nk);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+      __builtin_amdgcn_s_barrier();
+    }
+    if (active) {
+      bf16x8 kf[8];
+      kfrags(lk, kf);
+      floatx16 sa0, sa1, sb0, sb1;
+      scores(kf, qa, sa0, sa1);
+      scores(kf, qb, sb0, sb1);
+      if (nk < KT) {
+        mask(sa0, sa1, nk);
+        mask(sb0, sb1, nk);
+      }
+      bf16x8 pa[4], pbb[4];
+      softmax(sa0, sa1, ma, la, oa0, oa1, lk, qa, nk, j == 0, pa);
+      const uint16_t* lv = lk + TILE_ELEMS;
+      bf16x8 vf[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        vf[t] = lds_frag(lv, lr, 2 * t + lh);
+        vf[4 + t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) oa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pa[t], oa0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) oa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + t], pa[t], oa1, 0, 0, 0);
+      softmax(sb0, sb1, mb, lb, ob0, ob1, lk, qb, nk, j == 0, pbb);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ob0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pbb[t], ob0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ob1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + t], pbb[t], ob1, 0, 0, 0);
+    }
+    cursor_next(src, ee, cc);
+    ++j;
+  }
+
+  // ---- epilogue: each wave owns its rows; same output forms as attn_bf16_kernel
+  if (!active) return;
+  int t_end = tid;
+  asm volatile("" : "+v"(t_end));
+  const int lr2 = t_end & 31, lh2 = (t_end >> 5) & 1;
+  auto write_block = [&](int qrow, const floatx16& o0, const floatx16& o1, float m, float l) {
+    const float ltot = pair_sum(l);
+    if (qrow >= qn) return;  // (both lanes of a row pair share qrow)
+    const bool empty = !(ltot > 0.f);
+    const float inv = empty ? 0.f : 1.f / ltot;
+    const float lse_nat = empty ? -INFINITY : (m + __log2f(ltot)) * 0.69314718055994530942f;
+    const size_t orow = static_cast<size_t>(q0 + qrow) * H + h;
+    // 32x32 accumulator: element r of o0 is dim (r>>2)*8 + 4*lh + (r&3); o1 adds 32.
+    auto get = [&](int jj) { return jj < 16 ? o0[jj] : o1[jj - 16]; };
+    if (p.num_splits == 1) {
+      uint16_t* og = static_cast<uint16_t*>(p.o) + orow * D;
+#pragma unroll
+      for (int r4 = 0; r4 < 8; ++r4) {
+        floatx4 f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) f[jj] = get(r4 * 4 + jj) * inv;
+        *reinterpret_cast<bf16x4*>(og + r4 * 8 + 4 * lh2) = __builtin_convertvector(f, bf16x4);
+      }
+      if (p.lse && lh2 == 0) p.lse[orow] = lse_nat;
+    } else {
+      const size_t prow = static_cast<size_t>(split) * p.total_q * H + orow;
+      float amax = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) amax = fmaxf(amax, fabsf(get(jj) * inv));
+      amax = pair_max(amax);
+      int e2 = 0;
+      if (amax > 32768.f) {
+        int fe;
+        frexpf(amax, &fe);
+        e2 = fe - 15;
+      }
+      const float down = __builtin_ldexpf(inv, -e2);
+      _Float16* po = p.part_o16 + prow * D;
+#pragma unroll
+      for (int r4 = 0; r4 < 8; ++r4) {
+        floatx4 f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) f[jj] = get(r4 * 4 + jj) * down;
+        *reinterpret_cast<halfx4*>(po + r4 * 8 + 4 * lh2) = __builtin_convertvector(f, halfx4);
+      }
+      if (lh2 == 0) {
+        p.part_lse[prow] = lse_nat;
+        p.part_scale[prow] = __builtin_ldexpf(1.f, e2);
+      }
+    }
+  };
+  write_block(wrow0 + lr2, oa0, oa1, ma, la);
+  write_block(wrow0 + 32 + lr2, ob0, ob1, mb, lb);
+}
+
 }  // namespace
 
 // blocks <= 8: that many 32-row blocks; 9: eight blocks plus the shared 16-row
-// extra block.
-int attn_bf16_rows_per_tile(int blocks) { return blocks <= 8 ? blocks * 32 : 8 * 32 + 16; }
+// extra block; 10: sixteen blocks, two per wave (attn_wide_kernel).
+int attn_bf16_rows_per_tile(int blocks) { return blocks <= 8 ? blocks * 32 : blocks == 9 ? 8 * 32 + 16 : 512; }
 
 template <bool KV8, class Src>
 static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
@@ -1303,6 +1615,12 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
       break;
     case 9:
       hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 128), 0, stream, src);
+      break;
+    case 10:
+      if constexpr (KV8)
+        return hipErrorInvalidValue;  // 512-row tiles serve bf16 pages only
+      else
+        hipLaunchKernelGGL((attn_wide_kernel<Src>), grid, dim3(8 * 64), 0, stream, src);
       break;
     default:
       return hipErrorInvalidValue;

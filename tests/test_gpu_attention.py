@@ -136,11 +136,13 @@ def test_multi_sequence_ragged(dtype):
                 assert (to_f64(o[a:b]) == 0).all()
 
 
-@pytest.mark.parametrize("qn", [1, 32, 33, 100, 224, 256, 257, 262, 271, 272, 273, 288, 289, 545])
+@pytest.mark.parametrize("qn", [1, 32, 33, 100, 224, 256, 257, 262, 271, 272, 273, 288, 289, 545, 1025, 1100, 1536, 1600])
 def test_query_counts_across_tile_shapes(qn):
     """One sequence whose query count walks through every workgroup shape: 1..8
-    32-row blocks, the 272-row tile with its 16-row extra block, and a second
-    query tile; keys from ragged pages, with and without key splits."""
+    32-row blocks, the 272-row tile with its 16-row extra block, 256-row tiles
+    (the pipelined kernel) and 512-row tiles (two blocks per wave, above 1024
+    queries), with partial last tiles; keys from ragged pages, with and
+    without key splits."""
     import torch
     from paged_sliding_window_kv_amd import paged_attention
     log(f"query count {qn}")
@@ -168,18 +170,20 @@ def test_query_counts_across_tile_shapes(qn):
 
 
 @pytest.mark.parametrize("splits", [0, 1, 5])
-def test_256_row_tiles_short_and_empty_key_ranges(splits):
-    """256-row query tiles (the 8-wave software-pipelined kernel) against key
-    ranges that leave its pipeline nearly or entirely empty: no keys at all
-    (O = 0, lse = -inf), one token, one page shorter than a 64-key tile, one
-    exactly full tile, and a 5-page range whose forced splits leave whole
-    splits with a single tile; NaN-poisoned stale slots."""
+@pytest.mark.parametrize("wide", [False, True])
+def test_large_tiles_short_and_empty_key_ranges(splits, wide):
+    """256-row query tiles (the 8-wave software-pipelined kernel) and 512-row
+    tiles (two 32-row blocks per wave, above 1024 queries) against key ranges
+    that leave the key loop nearly or entirely empty: no keys at all (O = 0,
+    lse = -inf), one token, one page shorter than a 64-key tile, one exactly
+    full tile, and a 5-page range whose forced splits leave whole splits with
+    a single tile; NaN-poisoned stale slots."""
     import torch
     from paged_sliding_window_kv_amd import paged_attention
-    log(f"256-row tiles, short key ranges, splits={splits}")
+    log(f"large tiles (wide={wide}), short key ranges, splits={splits}")
     rng = np.random.default_rng(55)
     H, P, N = 2, 256, 16
-    qlens = [300, 257, 512, 300, 270]
+    qlens = [1100, 1025, 1600, 530, 1100] if wide else [300, 257, 512, 300, 270]
     page_lens = [[], [1], [37], [64], [256, 64, 200, 1, 65]]
     counts = [len(x) for x in page_lens]
     ids = rng.choice(N, size=sum(counts), replace=False).astype(np.int32)
@@ -212,7 +216,7 @@ def test_256_row_tiles_short_and_empty_key_ranges(splits):
             assert (to_f64(o[a:b]) == 0).all()
 
 
-@pytest.mark.parametrize("qn", [262, 256])
+@pytest.mark.parametrize("qn", [262, 256, 1100])
 def test_late_keys_outgrow_running_maximum(qn):
     """Scores of later pages exceed every earlier one by far more than 16 log2
     units, so the kernel's rescale path (tile maximum taken again, O and row sum

@@ -172,11 +172,11 @@ def test_split_choice_and_workspace():
     assert sz.value >= ns.value * 262 * 16 * 65 * 4
     a.num_splits = 1
     assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0 and sz.value == 0
-    # a 10,992-query chunk over 172 pages: 688 query tiles fill 2.69 rounds of the
-    # chip unsplit; 4 splits give 11 rounds, the last nearly full
+    # a 10,992-query chunk over 172 pages: 352 query tiles of 512 rows fill 1.375
+    # rounds of the chip unsplit; 5 splits give 7 rounds, the last 88% full
     a.num_splits, a.total_q, a.max_qo_len, a.max_kv_pages = 0, 10992, 10992, 172
-    assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 4
-    # 100 frames x 1374 queries over 537 pages: 8,592 tiles nearly fill 34 rounds, no split
+    assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 5
+    # 100 frames x 1374 queries over 537 pages: 4,304 tiles nearly fill 17 rounds, no split
     a.total_q, a.max_qo_len, a.max_kv_pages = 137400, 137400, 537
     assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 1
 
