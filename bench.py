@@ -491,7 +491,7 @@ def run_chunked(args) -> dict:
                    "keep_ratio": kr, "attended_tokens": lk},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "paged attention call (attn_pipe_kernel + attn_merge16_kernel)",
+                     "kernel": "paged attention call (attn_wide_kernel + attn_merge16_kernel)",
                      "avg_call_us": att / n * 1e6, "calls": n,
                      "bytes_per_call_avg": sum(attn_bytes(tokens, x, c["heads"]) for x in
                                                ([lk] * L if kr >= 1.0 else lks)) / L},
@@ -575,7 +575,7 @@ def run_global(args) -> dict:
                    "layers": L, "heads": H, "head_dim": 64, "tokens": T},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "global attention call (attn_pipe_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
+                     "kernel": "global attention call (attn_wide_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
                      "frame_attn_tflops": fl_f / tfr / 1e12},
     }
 
@@ -659,7 +659,7 @@ def main():
             res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "chunked":
         res = run_chunked(args)
-        ratio = measured_traffic_ratio("attn_pipe_vggt_chunked.md") if args.keep_ratio >= 1.0 else None
+        ratio = measured_traffic_ratio("attn_wide_vggt_chunked.md") if args.keep_ratio >= 1.0 else None
         if ratio is not None:
             res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
             res["roofline"]["traffic_ratio"] = ratio
