@@ -1283,10 +1283,11 @@ __global__ __launch_bounds__(512) void attn_pipe_kernel(const Src src) {
 // a barrier.  Here one wave serves two 32-row blocks with the same K and V
 // fragments, the same table walk and the same barrier, so that work is spent
 // once per 64 rows.  There is no cross-tile pipeline (the two blocks'
-// accumulators take the registers): within a tile, block B's score products
-// are issued between block A's exponentials, and block A's P V products
-// between block B's.  Numerics, ring, masking and output formats are those
-// of the other bf16 kernels.
+// accumulators take the registers).  Within a tile the score products of
+// both blocks are issued together, then block A's softmax and P V products,
+// then block B's, so that block A's products can run under block B's
+// softmax.  Numerics, ring, masking and output formats are those of the
+// other bf16 kernels.
 template <class Src>
 __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
   constexpr int W = 8;                   // waves, one per 64-row pair of blocks
