@@ -1,0 +1,68 @@
+"""Seeded random shapes against the fp64 oracle.
+
+Each case draws a batch of sequences whose query counts straddle every tile
+shape the library chooses (32-row blocks up to 256 queries, the 272-row tile,
+256-row pipelined tiles, 512-row tiles above 1024 queries), ragged page
+tables (lengths 1..P, empty sequences) with NaN-poisoned stale slots, 1 to 3
+heads, and forced or automatic key splits.  Page ids are distinct across the
+batch; the oracle gathers each sequence's keys from the same pool bits and
+computes fp64 attention.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import check_attention, log, to_dev, to_f64, v_pool_device_layout, v_positions
+from oracle import attention_f64
+from oracle import to_f64 as bits_f64
+
+pytestmark = pytest.mark.gpu
+
+# query counts around each tile-shape boundary
+_QN = [1, 31, 32, 200, 256, 257, 262, 272, 273, 300, 511, 512, 513, 1024, 1025, 1300, 1537]
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_batches_against_oracle(case):
+    import torch
+    from paged_sliding_window_kv_amd import paged_attention
+    rng = np.random.default_rng(9000 + case)
+    H = int(rng.integers(1, 4))
+    P, N = 256, 48
+    nseq = int(rng.integers(1, 4))
+    qlens = [int(rng.choice(_QN)) for _ in range(nseq)]
+    counts = [int(rng.integers(0, 6)) for _ in range(nseq)]
+    if sum(counts) == 0:
+        counts[0] = 1
+    ids = rng.choice(N, size=sum(counts), replace=False).astype(np.int32)
+    lens = rng.integers(1, P + 1, size=sum(counts)).astype(np.int32)
+    full = rng.random(sum(counts)) < 0.5
+    lens[full] = P  # half the pages full, as in a stream
+    kv = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    splits = int(rng.choice([0, 0, 1, 2, 3, 7]))
+    log(f"case {case}: H={H} qlens={qlens} pages={counts} splits={splits}")
+    kpool = synth.normal_tokens(11, case, 0, 1, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    vpool = synth.normal_tokens(11, case, 0, 2, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
+    q = synth.normal_tokens(11, case, 0, 0, int(qo[-1]), H, 64, "bf16")
+    kd = to_dev(kpool, "bf16")
+    vd = to_dev(v_pool_device_layout(vpool), "bf16")
+    pos = torch.from_numpy(v_positions(P)).cuda()
+    for p_, n in zip(ids, lens):
+        kd[p_, :, n:] = float("nan")
+        vd[p_][:, :, pos[n:]] = float("nan")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    o, lse = paged_attention(to_dev(q, "bf16"), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
+                             max_qo_len=max(qlens), max_kv_pages=max(counts), num_splits=splits)
+    for s_ in range(nseq):
+        a, b = qo[s_], qo[s_ + 1]
+        sel = list(zip(ids[kv[s_]:kv[s_ + 1]], lens[kv[s_]:kv[s_ + 1]]))
+        if sel:
+            gk = np.concatenate([kpool[p_, :, :n] for p_, n in sel], axis=1)
+            gv = np.concatenate([vpool[p_, :, :n] for p_, n in sel], axis=1)
+        else:
+            gk = gv = np.zeros((H, 0, 64), kpool.dtype)
+        ro, rl = attention_f64(bits_f64(q[a:b]), bits_f64(gk), bits_f64(gv))
+        check_attention(o[a:b], lse[a:b], ro, rl, "bf16", f"case {case} seq={s_} q={b - a} Lk={gk.shape[1]}")
+        if not sel:
+            assert (to_f64(o[a:b]) == 0).all()
