@@ -593,9 +593,13 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
 
 
 def attn_source_hash() -> str:
+    """Hash of the attention kernels' source and of the build script (whose flags shape the generated code)."""
     import hashlib
-    with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", "csrc", "attn_bf16.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in (("csrc", "attn_bf16.hip"), ("build.py",)):
+        with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", *rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic_ratio(name: str):

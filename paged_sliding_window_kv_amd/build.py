@@ -50,6 +50,10 @@ def compile_one(src: str, debug: bool) -> str:
             # The kernel never tests for NaN (masked keys are selected to -inf, and
             # infinities stay honoured), so max() needs no NaN-quieting of its inputs.
             cmd.append("-fno-honor-nans")
+            # The attention kernels are bound by instruction issue; the
+            # iterative ILP scheduling strategy measured 1-2% faster on the
+            # chunked and global calls (same source, no spills).
+            cmd += ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
     else:
         cmd = ["g++", src, "-c", "-o", obj] + common_flags(debug)
     r = subprocess.run(cmd, capture_output=True, text=True)
