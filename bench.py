@@ -14,6 +14,9 @@ Other workloads (--workload): "chunked" is VGGT-style chunked global attention
 attention over 100 frames x 1374 tokens followed by per-frame attention.
 "stream_batched" runs --batch LingBot streams side by side: per layer and frame,
 each stream appends its frame and one launch serves all streams' attention.
+"keyframe" is a small fp32 stream over 10,000 frames that keeps every fourth
+frame and rolls the others back; it reports frames/s and checks that device
+memory and the patch-page count stay constant.
 """
 from __future__ import annotations
 
@@ -580,6 +583,115 @@ def run_global(args) -> dict:
     }
 
 
+KEYFRAME = dict(heads=4, d=64, page=256, patch=256, special=6, scale=2, window=4, interval=4, frames=10000)
+
+
+def keyframe_kept(t: int, c=KEYFRAME) -> bool:
+    """Frame t's unit stays in the cache: the scale frames, then every interval-th frame."""
+    return t < c["scale"] or (t - c["scale"]) % c["interval"] == 0
+
+
+def run_keyframe(args) -> dict:
+    """Keyframe stream: 1 layer, 4 heads x 64, fp32 pages, 2 scale + 4 window frames, keyframe interval 4.
+
+    Each frame appends its unit, attends its 262 queries and, unless it is a
+    keyframe, rolls the append back (10,000 frames, 7,500 rollbacks).  The step
+    is the whole frame: host page bookkeeping, append kernel, attention.
+    """
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, lib
+    c = KEYFRAME
+    frames = args.steps
+    tok, H, d = c["patch"] + c["special"], c["heads"], c["d"]
+    log(f"[bench] keyframe: 1 layer, {frames} frames, interval {c['interval']}, warmup {args.warmup}")
+    dev = torch.device("cuda:0")
+    cache = KvCache(num_heads=H, head_dim=d, page_size=c["page"], dtype="f32", patch_tokens=c["patch"],
+                    special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
+                    max_units=frames, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bank = 4
+    q, k, v = (torch.randn((bank, tok, H, d), generator=g, device=dev, dtype=torch.float32) for _ in range(3))
+    o = torch.empty((tok, H, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((tok, H), dtype=torch.float32, device=dev)
+    wsb = cache.workspace_bytes(tok)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    L = lib()
+    h, sp = cache.handle, torch.cuda.current_stream(dev).cuda_stream
+    fb = tok * H * d * 4
+    qp = [q.data_ptr() + i * fb for i in range(bank)]
+    kp = [k.data_ptr() + i * fb for i in range(bank)]
+    vp = [v.data_ptr() + i * fb for i in range(bank)]
+    op, lp, wsp = o.data_ptr(), lse.data_ptr(), ws.data_ptr()
+
+    def frame(t, ev=None):
+        b = t % bank
+        _ok(L.kvc_append_frame(h, kp[b], vp[b], sp), "kvc_append_frame")
+        if ev is not None:
+            ev[0].record()
+        _ok(L.kvc_attend(h, qp[b], tok, 0.0, op, lp, wsp, wsb, sp), "kvc_attend")
+        if ev is not None:
+            ev[1].record()
+        if not keyframe_kept(t):
+            _ok(L.kvc_rollback_last_frame(h), "kvc_rollback_last_frame")
+
+    for t in range(min(args.warmup, frames)):
+        frame(t)
+    torch.cuda.synchronize()
+    cache.reset()
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    t0 = time.perf_counter()
+    for t in range(frames):
+        frame(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mem1 = torch.cuda.memory_allocated(dev)
+    st = cache.state()
+    # visible tokens when frame t attends: its own unit plus the units kept before it
+    total_flops, lks, kept = 0.0, [], 0
+    for t in range(frames):
+        u = kept + 1
+        lk = (min(u, c["scale"]) + min(max(u - c["scale"], 0), c["window"])) * c["patch"] + u * c["special"]
+        lks.append(lk)
+        total_flops += attn_flops(tok, lk, H, d)
+        kept += keyframe_kept(t)
+    assert st["num_units"] == kept, (st["num_units"], kept)
+    assert len(st["scale_pages"]) + len(st["window_pages"]) == c["scale"] + c["window"]
+    assert mem1 == mem0, (mem0, mem1)
+    fps = frames / elapsed
+    log(f"[bench] keyframe: {frames} frames in {elapsed:.3f} s, {fps:.0f} frames/s, "
+        f"{total_flops / elapsed / 1e12:.2f} TFLOP/s; {kept} units kept, device memory unchanged")
+    # attention calls alone, replayed with events around each call
+    cache.reset()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+    att = 0.0
+    for t0_ in range(0, frames, len(evs)):
+        n = min(len(evs), frames - t0_)
+        for i in range(n):
+            frame(t0_ + i, evs[i])
+        torch.cuda.synchronize()
+        att += sum(evs[i][0].elapsed_time(evs[i][1]) for i in range(n)) * 1e-3
+    ach = total_flops / att / 1e12
+    log(f"[bench] keyframe attention calls: {att / frames * 1e6:.2f} us avg, {ach:.2f} TFLOP/s (fp32 MFMA)")
+    peak_f32 = 157.3  # MI355X dense fp32 MFMA
+    return {
+        "value": fps, "unit": "frames/s", "ms_per_step": elapsed / frames * 1e3, "frames_per_s": fps,
+        "dtype": "f32",
+        "pct_bf16_mfma_peak": None,
+        "config": {"workload": f"keyframe_stream: 1 layer cache, {H} heads x {d}, fp32, 256 patch + 6 special "
+                               f"tokens/frame, {c['scale']} scale frames, {c['window']}-frame window, keyframe "
+                               f"every {c['interval']} frames (others rolled back), 262 queries/step, {frames} frames",
+                   "layers": 1, "heads": H, "head_dim": d, "page_size": c["page"], "frames": frames,
+                   "units_kept": kept, "rollbacks": frames - kept, "max_visible_tokens": max(lks),
+                   "tflops_whole_step": total_flops / elapsed / 1e12,
+                   "device_memory_growth_bytes": mem1 - mem0},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": peak_f32, "unit": "TFLOP/s", "frac": ach / peak_f32,
+                     "traffic": None, "kernel": "attn_f32_kernel (+ attn_merge_kernel when split)",
+                     "avg_call_us": att / frames * 1e6, "calls": frames},
+    }
+
+
 def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
     """A plain device-to-device copy of known size (reference for the FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -631,7 +743,8 @@ def main():
                     help="timed steps: frames (stream, default 1000), chunk steps (chunked, default 8) or "
                          "passes (global, default 1)")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stream", choices=["stream", "chunked", "global", "stream_batched"])
+    ap.add_argument("--workload", default="stream",
+                    choices=["stream", "chunked", "global", "stream_batched", "keyframe"])
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
@@ -654,7 +767,8 @@ def main():
         copy_probe()
         return
     if args.steps is None:
-        args.steps = {"stream": 1000, "chunked": 8, "global": 1, "stream_batched": 1000}[args.workload]
+        args.steps = {"stream": 1000, "chunked": 8, "global": 1, "stream_batched": 1000,
+                      "keyframe": KEYFRAME["frames"]}[args.workload]
     if args.workload == "stream":
         res = run_stream(args)
         ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md") if args.kv_dtype == "bf16" else None
@@ -669,6 +783,8 @@ def main():
             res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "stream_batched":
         res = run_stream_batched(args)
+    elif args.workload == "keyframe":
+        res = run_keyframe(args)
     else:
         res = run_global(args)
     out = {
@@ -682,7 +798,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": res.get("dtype", "bf16"),
         "data": "synthetic (seeded N(0,1) Q/K/V drawn on the device)",
         "config": res["config"],
         "frames_per_s": res["frames_per_s"],
