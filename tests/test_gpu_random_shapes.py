@@ -1,8 +1,9 @@
 """Seeded random shapes against the fp64 oracle.
 
 Each case draws a batch of sequences whose query counts straddle every tile
-shape the library chooses (32-row blocks up to 256 queries, the 272-row tile,
-256-row pipelined tiles, 512-row tiles above 1024 queries), ragged page
+shape the library chooses (bf16: 32-row blocks up to 256 queries, the 272-row
+tile, 256-row pipelined tiles, 512-row tiles above 1024 queries; fp32: 64-row
+tiles of two 32-row blocks), ragged page
 tables (lengths 1..P, empty sequences) with NaN-poisoned stale slots, 1 to 3
 heads, and forced or automatic key splits.  Page ids are distinct across the
 batch; the oracle gathers each sequence's keys from the same pool bits and
@@ -22,11 +23,11 @@ pytestmark = pytest.mark.gpu
 _QN = [1, 31, 32, 200, 256, 257, 262, 272, 273, 300, 511, 512, 513, 1024, 1025, 1300, 1537]
 
 
-@pytest.mark.parametrize("case", range(8))
-def test_random_batches_against_oracle(case):
+@pytest.mark.parametrize("dtype,case", [("bf16", c) for c in range(8)] + [("f32", c) for c in range(4)])
+def test_random_batches_against_oracle(dtype, case):
     import torch
     from paged_sliding_window_kv_amd import paged_attention
-    rng = np.random.default_rng(9000 + case)
+    rng = np.random.default_rng((9000 if dtype == "bf16" else 9100) + case)
     H = int(rng.integers(1, 4))
     P, N = 256, 48
     nseq = int(rng.integers(1, 4))
@@ -41,18 +42,18 @@ def test_random_batches_against_oracle(case):
     kv = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     qo = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     splits = int(rng.choice([0, 0, 1, 2, 3, 7]))
-    log(f"case {case}: H={H} qlens={qlens} pages={counts} splits={splits}")
-    kpool = synth.normal_tokens(11, case, 0, 1, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
-    vpool = synth.normal_tokens(11, case, 0, 2, N * H * P, 1, 64, "bf16").reshape(N, H, P, 64)
-    q = synth.normal_tokens(11, case, 0, 0, int(qo[-1]), H, 64, "bf16")
-    kd = to_dev(kpool, "bf16")
-    vd = to_dev(v_pool_device_layout(vpool), "bf16")
+    log(f"{dtype} case {case}: H={H} qlens={qlens} pages={counts} splits={splits}")
+    kpool = synth.normal_tokens(11, case, 0, 1, N * H * P, 1, 64, dtype).reshape(N, H, P, 64)
+    vpool = synth.normal_tokens(11, case, 0, 2, N * H * P, 1, 64, dtype).reshape(N, H, P, 64)
+    q = synth.normal_tokens(11, case, 0, 0, int(qo[-1]), H, 64, dtype)
+    kd = to_dev(kpool, dtype)
+    vd = to_dev(v_pool_device_layout(vpool), dtype)
     pos = torch.from_numpy(v_positions(P)).cuda()
     for p_, n in zip(ids, lens):
         kd[p_, :, n:] = float("nan")
         vd[p_][:, :, pos[n:]] = float("nan")
     dev = lambda a: torch.from_numpy(a).cuda()
-    o, lse = paged_attention(to_dev(q, "bf16"), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
+    o, lse = paged_attention(to_dev(q, dtype), kd, vd, dev(ids), dev(lens), dev(qo), dev(kv),
                              max_qo_len=max(qlens), max_kv_pages=max(counts), num_splits=splits)
     for s_ in range(nseq):
         a, b = qo[s_], qo[s_ + 1]
@@ -63,6 +64,6 @@ def test_random_batches_against_oracle(case):
         else:
             gk = gv = np.zeros((H, 0, 64), kpool.dtype)
         ro, rl = attention_f64(bits_f64(q[a:b]), bits_f64(gk), bits_f64(gv))
-        check_attention(o[a:b], lse[a:b], ro, rl, "bf16", f"case {case} seq={s_} q={b - a} Lk={gk.shape[1]}")
+        check_attention(o[a:b], lse[a:b], ro, rl, dtype, f"{dtype} case {case} seq={s_} q={b - a} Lk={gk.shape[1]}")
         if not sel:
             assert (to_f64(o[a:b]) == 0).all()
