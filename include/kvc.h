@@ -155,7 +155,8 @@ int kvc_destroy(kvc_t* cache);
  * section 3.3: KV append, then eviction of the oldest chunk beyond the
  * window).  k_unit / v_unit: device [patch_tokens + special_tokens][H][d],
  * patch tokens first, in the cache dtype (bf16 for FP8 caches, quantised by
- * the append); both NULL on a host-only handle.
+ * the append); both NULL on a host-only handle.  Both 16-byte aligned
+ * (KVC_ERR_INVALID_ARGUMENT otherwise).
  * Plans on the host and enqueues one scatter kernel on `stream`.
  * KVC_ERR_OUT_OF_PAGES when the free list cannot supply the unit. */
 int kvc_append_frame(kvc_t* cache, const void* k_unit, const void* v_unit, kvc_stream_t stream);
@@ -209,6 +210,8 @@ typedef struct paged_attn_args {
   void* o;                  /* device [total_q][H][d]; rows of a sequence with no keys are 0 */
   float* lse;               /* device [total_q][H] natural-log sum of exp of scaled scores, or NULL */
   void* workspace;          /* device scratch of paged_attn_workspace_size bytes (NULL if 0) */
+                            /* q, k_pool, v_pool, o and workspace must be 16-byte aligned
+                               (KVC_ERR_INVALID_ARGUMENT otherwise) */
   size_t workspace_bytes;
 } paged_attn_args;
 

@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -143,6 +144,11 @@ int check_attn_args(const paged_attn_args* a) {
     return fail(KVC_ERR_INVALID_ARGUMENT, "negative size in paged_attn_args");
   if (!(std::isfinite(a->sm_scale) && a->sm_scale > 0.f))
     return fail(KVC_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+  // the kernels move q, the pools, o and the split partials in 16-byte accesses
+  const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k_pool) |
+                         reinterpret_cast<uintptr_t>(a->v_pool) | reinterpret_cast<uintptr_t>(a->o) |
+                         reinterpret_cast<uintptr_t>(a->workspace);
+  if (ptrs & 15) return fail(KVC_ERR_INVALID_ARGUMENT, "q, k_pool, v_pool, o and workspace must be 16-byte aligned");
   return KVC_OK;
 }
 
@@ -224,6 +230,8 @@ int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_strea
   const bool device = c->k_pool != nullptr;
   if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
   if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
+  if ((reinterpret_cast<uintptr_t>(k_unit) | reinterpret_cast<uintptr_t>(v_unit)) & 15)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
   kvc::AppendPlan plan;
   const int s = c->pc.append(device ? &plan : nullptr);
   if (s != KVC_OK) return fail(s, "append needs %d pages", c->pc.unit_pages());

@@ -87,19 +87,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int parts, int rows_hea
 // The same merge over partials in the fp16 form of the bf16 and FP8 attention
 // kernels: part i holds O_i * 2^-E_i in fp16 and 2^E_i in part_scale, so its
 // term is exp(lse_i - lse) * 2^E_i * (stored values).  Output bf16.
+// fp16 partials: one thread per (row, head, 8 dims), so each part's O is one
+// 16-byte load per thread (half the threads and loads of a 4-dim split,
+// measured 0.65 us less per LingBot-frame call).
+typedef _Float16 halfx8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef float floatx8 __attribute__((__vector_size__(8 * sizeof(float))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 __global__ __launch_bounds__(256) void attn_merge16_kernel(int parts, int rows_heads, const _Float16* __restrict__ po,
                                                            const float* __restrict__ pscale,
                                                            const float* __restrict__ plse, uint16_t* __restrict__ o,
                                                            float* __restrict__ lse) {
-  const int rh = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int d4 = (threadIdx.x & 15) * 4;
+  const int rh = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int d8 = (threadIdx.x & 7) * 8;
   if (rh >= rows_heads) return;
   constexpr int B = 16;
   float m = -INFINITY, z = 0.f;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  floatx8 acc = {};
   for (int i0 = 0; i0 < parts; i0 += B) {
     float li[B], si[B];
-    halfx4 oi[B];
+    halfx8 oi[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int i = i0 + j;
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void attn_merge16_kernel(int parts, int rows_h
       const size_t r = static_cast<size_t>(i) * rows_heads + rh;
       li[j] = ok ? plse[r] : -INFINITY;
       si[j] = ok ? pscale[r] : 0.f;
-      oi[j] = ok ? *reinterpret_cast<const halfx4*>(po + r * D + d4) : halfx4{};
+      oi[j] = ok ? *reinterpret_cast<const halfx8*>(po + r * D + d8) : halfx8{};
     }
     float mb = li[0];
 #pragma unroll
@@ -124,16 +130,16 @@ __global__ __launch_bounds__(256) void attn_merge16_kernel(int parts, int rows_h
       const float w = li[j] == -INFINITY ? 0.f : __expf(li[j] - m);
       z += w;
       const float ws = w * si[j];
-      const floatx4 f = __builtin_convertvector(oi[j], floatx4);
+      const floatx8 f = __builtin_convertvector(oi[j], floatx8);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(ws, f[k], acc[k]);
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(ws, f[k], acc[k]);
     }
   }
-  floatx4 out;
+  floatx8 out;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) out[k] = z > 0.f ? acc[k] / z : 0.f;
-  store_out<uint16_t>(o, static_cast<size_t>(rh) * D + d4, out);
-  if (lse && d4 == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
+  for (int k = 0; k < 8; ++k) out[k] = z > 0.f ? acc[k] / z : 0.f;
+  *reinterpret_cast<bf16x8*>(o + static_cast<size_t>(rh) * D + d8) = __builtin_convertvector(out, bf16x8);
+  if (lse && d8 == 0) lse[rh] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
 }  // namespace
@@ -157,7 +163,7 @@ hipError_t launch_attn_merge16(int num_parts, int rows, int num_heads, const _Fl
                                hipStream_t stream) {
   const int rh = rows * num_heads;
   if (rh == 0) return hipSuccess;
-  const dim3 grid((rh + 15) / 16);
+  const dim3 grid((rh + 31) / 32);
   hipLaunchKernelGGL(attn_merge16_kernel, grid, dim3(256), 0, stream, num_parts, rh, part_o16, part_scale, part_lse,
                      static_cast<uint16_t*>(o), lse);
   return hipGetLastError();

@@ -157,6 +157,14 @@ def test_error_paths():
     a.head_dim = 64
     a.sm_scale = float("nan")
     assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT
+    # device pointers must be 16-byte aligned (checked before any device work)
+    a.sm_scale = 0.125
+    assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0
+    for field in ("q", "k_pool", "v_pool", "o", "workspace"):
+        setattr(a, field, C.c_void_p(4096 + 8))
+        assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT, field
+        setattr(a, field, C.c_void_p(4096))
+        assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0, field
 
 
 def test_split_choice_and_workspace():
