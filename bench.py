@@ -422,8 +422,8 @@ def run_chunked(args) -> dict:
     log(f"[bench] chunked: {L} layers, chunk {tokens} tokens, window {W} chunks, warmup {warm}, timed {steps}")
     dev = torch.device("cuda:0")
     lb = lib()
-    caches = [KvCache(num_heads=c["heads"], dtype="bf16", patch_tokens=tokens, special_tokens=0, num_scale_units=0,
-                      window_units=W, max_units=warm + steps, device=dev) for _ in range(L)]
+    caches = [KvCache(num_heads=c["heads"], dtype=args.kv_dtype, patch_tokens=tokens, special_tokens=0,
+                      num_scale_units=0, window_units=W, max_units=warm + steps, device=dev) for _ in range(L)]
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     bank = 2
@@ -486,18 +486,20 @@ def run_chunked(args) -> dict:
         "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3,
         "frames_per_s": steps * c["frames_per_chunk"] / el,
         "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
-        "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, bf16, chunks of 8 x 1374 = {tokens} "
+        "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, {kv_label(args.kv_dtype)}, "
+                               f"chunks of 8 x 1374 = {tokens} "
                                f"tokens, window 4 chunks ({W * tokens} visible keys)"
                                + (f", per-layer page subsets keeping {kr} ({lk:.0f} keys attended)" if kr < 1.0 else "")
                                + f", {steps} timed chunk steps",
                    "layers": L, "heads": 16, "head_dim": 64, "chunk_tokens": tokens, "visible_tokens": W * tokens,
-                   "keep_ratio": kr, "attended_tokens": lk},
+                   "keep_ratio": kr, "attended_tokens": lk, "kv_dtype": args.kv_dtype},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "paged attention call (attn_wide_kernel + attn_merge16_kernel)",
+                     "kernel": "paged attention call (attn_wide_kernel + attn_merge16_kernel)" if args.kv_dtype == "bf16"
+                               else "paged attention call (attn_bf16_kernel<KV8> + attn_merge16_kernel)",
                      "avg_call_us": att / n * 1e6, "calls": n,
-                     "bytes_per_call_avg": sum(attn_bytes(tokens, x, c["heads"]) for x in
-                                               ([lk] * L if kr >= 1.0 else lks)) / L},
+                     "bytes_per_call_avg": sum(attn_bytes(tokens, x, c["heads"], kv_elem=kv_elem_bytes(args.kv_dtype))
+                                               for x in ([lk] * L if kr >= 1.0 else lks)) / L},
     }
 
 
@@ -748,7 +750,8 @@ def main():
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
-                    help="stream: KV page type (fp8 = E4M3 codes with per-token exponents, RFC section 3.4)")
+                    help="stream and chunked: KV page type (fp8 = E4M3 codes with per-token exponents, "
+                         "RFC section 3.4)")
     ap.add_argument("--keep-ratio", type=float, default=1.0,
                     help="chunked: attend to a per-layer random page subset keeping this fraction (AVGGT-style)")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
@@ -777,7 +780,8 @@ def main():
             res["roofline"]["traffic_ratio"] = ratio
     elif args.workload == "chunked":
         res = run_chunked(args)
-        ratio = measured_traffic_ratio("attn_wide_vggt_chunked.md") if args.keep_ratio >= 1.0 else None
+        ratio = (measured_traffic_ratio("attn_wide_vggt_chunked.md")
+                 if args.keep_ratio >= 1.0 and args.kv_dtype == "bf16" else None)
         if ratio is not None:
             res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
             res["roofline"]["traffic_ratio"] = ratio

@@ -59,9 +59,11 @@ int choose_waves(const paged_attn_args& a) {
   // when they need at least 10% fewer query tiles than 256-row ones (a frame of
   // 262 queries: one tile instead of two); otherwise 256-row workgroups, whose
   // per-step work is even across the waves (measured 9% faster on 10,992-row
-  // chunks, where the tile counts are 41 and 43).
+  // chunks, where the tile counts are 41 and 43).  Above 1,024 queries, bf16
+  // and FP8 pages take 512-row tiles (returned as 10: eight waves, two 32-row
+  // blocks each).
   const long q = a.max_qo_len;
-  if (a.dtype == KVC_DTYPE_BF16 && q > 1024) return 10;
+  if (a.dtype != KVC_DTYPE_F32 && q > 1024) return 10;
   if (q <= 256) return std::max(1, static_cast<int>((q + 31) / 32));
   const long t272 = (q + 271) / 272, t256 = (q + 255) / 256;
   return 10 * t256 >= 11 * t272 ? 9 : 8;

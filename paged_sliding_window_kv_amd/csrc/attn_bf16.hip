@@ -1287,15 +1287,23 @@ __global__ __launch_bounds__(512) void attn_pipe_kernel(const Src src) {
 // both blocks are issued together, then block A's softmax and P V products,
 // then block B's, so that block A's products can run under block B's
 // softmax.  Numerics, ring, masking and output formats are those of the
-// other bf16 kernels.
-template <class Src>
+// other bf16 kernels.  With FP8 pages (KV8) the ring stages codes and row
+// exponents; at iteration j the workgroup converts tile j+1 into one of two
+// bf16 tiles (as attn_bf16_kernel does for its pairs) before the products on
+// tile j, and the next barrier publishes it.
+template <class Src, bool KV8 = false>
 __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
   constexpr int W = 8;                   // waves, one per 64-row pair of blocks
   constexpr int ROWS = W * 64;
   constexpr int LPT = DMA_PER_TILE / W;  // direct loads per wave per tile
-  constexpr int SMEM = STAGES * 2 * TILE_ELEMS * 2;
+  constexpr int TILE_BYTES = 2 * TILE_ELEMS * 2;   // K and V^T of one bf16 tile
+  constexpr int STAGE8 = 2 * TILE_ELEMS + 2 * KT;  // FP8 stage: K codes, V codes, K exps, V exps
+  // bf16 pages: the ring of bf16 tiles.  FP8 pages: two converted bf16 tiles
+  // (tile j in buffer j % 2), then the ring of FP8 stages.
+  constexpr int SMEM = KV8 ? 2 * TILE_BYTES + STAGES * STAGE8 : STAGES * TILE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   uint16_t* const lds_t = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* const lds8 = smem + (KV8 ? 2 * TILE_BYTES : 0);
   const AttnParams& p = attn_base(src);
 
   // ---- which (sequence, head, split, query tile): as attn_bf16_kernel -----
@@ -1359,13 +1367,77 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
     dma_goff[j] = is_v ? row * P + chunk * 8 : row * D + chunk * 8;
     dma_loff[j] = is_v * TILE_ELEMS + part * 512;
   }
-  auto issue = [&](const Cursor& c, int stage) {
-    const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
-    const int koff = c.kt * KT * D, voff = c.kt * KT;
+  // FP8 loads (as attn_bf16_kernel): inst 0-3 K codes (1 KiB each), 4-7 V
+  // codes, 8-11 K exponents and 12-15 V exponents (16 bytes, lane 0 only).
+  int dma8_kind[LPT], dma8_off[LPT];
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
-      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_t + stage * 2 * TILE_ELEMS + dma_loff[j]), 16, 0, 0);
+  for (int j = 0; j < LPT; ++j) {
+    const int inst = wave * LPT + j;
+    const int kind = inst >> 2, q = inst & 3;
+    dma8_kind[j] = kind;
+    dma8_off[j] = kind < 2 ? kind * 4096 + q * 1024 : 8192 + (kind - 2) * KT + q * 16;
+  }
+  const uint8_t* __restrict__ kg8 = static_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* __restrict__ vg8 = static_cast<const uint8_t*>(p.v_pool);
+  const size_t codes_bytes = static_cast<size_t>(p.num_pool_pages) * H * P * D;  // exponents follow
+  auto issue = [&](const Cursor& c, int stage) {
+    if constexpr (KV8) {
+      const size_t row0 = (static_cast<size_t>(c.pid) * H + h) * P + c.kt * KT;  // first slot row of the tile
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int kind = dma8_kind[j];
+        const uint8_t* base = (kind & 1) ? vg8 : kg8;
+        if (kind < 2) {
+          const void* gp = base + row0 * D + (dma8_off[j] & 4095) + lane * 16;
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds8 + stage * STAGE8 + dma8_off[j]), 16, 0, 0);
+        } else if (lane == 0) {
+          const void* gp = base + codes_bytes + row0 + (dma8_off[j] - 8192 - (kind - 2) * KT);
+          __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds8 + stage * STAGE8 + dma8_off[j]), 16, 0, 0);
+        }
+      }
+    } else {
+      const size_t base = static_cast<size_t>(c.pid) * page_stride + head_off;
+      const int koff = c.kt * KT * D, voff = c.kt * KT;
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const uint16_t* gp = (dma_v[j] ? vg + voff : kg + koff) + base + dma_goff[j];
+        __builtin_amdgcn_global_load_lds(gp, (lds_void*)(lds_t + stage * 2 * TILE_ELEMS + dma_loff[j]), 16, 0, 0);
+      }
+    }
+  };
+  // FP8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`
+  // (as attn_bf16_kernel): K rows keep their layout, V rows become V^T rows in
+  // the pool slot order with the chunk swizzle, keys past nk become zeros.
+  auto convert = [&](int stage, int b, int nk) {
+    const uint8_t* st8 = lds8 + stage * STAGE8;
+    uint16_t* tk = lds_t + b * 2 * TILE_ELEMS;
+    int t0 = tid;
+    asm volatile("" : "+v"(t0));
+    for (int it = t0; it < 2 * KT * 8; it += W * 64) {
+      const bool is_v = it >= KT * 8;
+      const int r = (it >> 3) & (KT - 1), ch = it & 7;  // token, 8-dim chunk
+      const uint2 w = *reinterpret_cast<const uint2*>(st8 + (is_v ? 4096 : 0) + r * D + ch * 8);
+      const int e = static_cast<int8_t>(st8[8192 + (is_v ? KT : 0) + r]);
+      const float sc = __builtin_ldexpf(1.f, e);
+      bf16x2 v2[4];
+      v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, false);
+      v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, true);
+      v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, false);
+      v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, true);
+      uint32_t u[4];
+      __builtin_memcpy(u, v2, sizeof u);
+      if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
+      if (!is_v) {
+        *reinterpret_cast<uint4*>(tk + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
+      } else {
+        const int pos = v_slot_pos(r);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int row = ch * 8 + jj;  // dim
+          tk[TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
+              static_cast<uint16_t>(u[jj >> 1] >> (16 * (jj & 1)));
+        }
+      }
     }
   };
   // Waits for this wave's loads of all tiles but the last `ahead` issued.
@@ -1395,7 +1467,7 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
         if (k0 + e >= nk) rp[e] = 0;
     }
   };
-  auto stage_ptr = [&](int t) { return lds_t + (t % STAGES) * 2 * TILE_ELEMS; };
+  auto stage_ptr = [&](int t) { return lds_t + (KV8 ? (t & 1) : t % STAGES) * 2 * TILE_ELEMS; };
   // Keys nk..63 get -inf scores (32x32 layout: element r of s0 is key
   // (r>>2)*8 + 4lh + (r&3), s1 adds 32); the lane threshold is formed at each
   // call so that no per-element key indices stay live across the loop.
@@ -1480,11 +1552,28 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
     cursor_next(src, ee, lc);
     ++ni;
   }
+  if constexpr (KV8) {
+    // FP8: tile 0 is converted here; at iteration j the workgroup converts
+    // tile j+1 into the other buffer before its products on tile j, so one
+    // barrier per tile publishes both the next bf16 tile and the free stage.
+    if (ni > 0) {
+      wait_tiles(ni - 1);
+      __builtin_amdgcn_s_barrier();
+      convert(0, 0, min(KT, cc.len - cc.kt * KT));
+    }
+  }
   while (cc.e < ee) {
-    wait_tiles(ni - (j + 1));  // tile j
+    Cursor cn = cc;  // tile j+1 (FP8: converted in this iteration)
+    if constexpr (KV8) {
+      cursor_next(src, ee, cn);
+      wait_tiles(ni - (j + 2));  // tile j+1
+    } else {
+      wait_tiles(ni - (j + 1));  // tile j
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
     __builtin_amdgcn_s_barrier();
-    // Stage (j-1) % STAGES is free (every wave is past iteration j-1).
+    // Stage (j-1) % STAGES is free (every wave is past iteration j-1; FP8:
+    // that stage was converted at iteration j-2).
     if (lc.e < ee) {
       issue(lc, ni % STAGES);
       cursor_next(src, ee, lc);
@@ -1492,7 +1581,10 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
     }
     const int nk = min(KT, cc.len - cc.kt * KT);
     uint16_t* const lk = stage_ptr(j);
-    if (nk < KT) {  // rare: a page's last, partial tile
+    if constexpr (KV8) {
+      // Buffer (j+1) % 2 was last read at iteration j-1 (barrier above).
+      if (cn.e < ee) convert((j + 1) % STAGES, (j + 1) & 1, min(KT, cn.len - cn.kt * KT));
+    } else if (nk < KT) {  // rare: a page's last, partial tile
       zero_tail(lk + TILE_ELEMS, nk);
       __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
       __builtin_amdgcn_s_barrier();
@@ -1618,10 +1710,7 @@ static hipError_t launch_impl(const Src& src, int waves, hipStream_t stream) {
       hipLaunchKernelGGL((attn_bf16_kernel<8, true, Src, KV8>), grid, dim3(8 * 128), 0, stream, src);
       break;
     case 10:
-      if constexpr (KV8)
-        return hipErrorInvalidValue;  // 512-row tiles serve bf16 pages only
-      else
-        hipLaunchKernelGGL((attn_wide_kernel<Src>), grid, dim3(8 * 64), 0, stream, src);
+      hipLaunchKernelGGL((attn_wide_kernel<Src, KV8>), grid, dim3(8 * 64), 0, stream, src);
       break;
     default:
       return hipErrorInvalidValue;
