@@ -1405,37 +1405,55 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
       }
     }
   };
-  // FP8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`
-  // (as attn_bf16_kernel): K rows keep their layout, V rows become V^T rows in
-  // the pool slot order with the chunk swizzle, keys past nk become zeros.
+  // FP8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`.
+  // K: one thread per (token, 8-dim chunk), a 16-byte row write.  V: one
+  // thread per (4 consecutive tokens, 8-dim chunk); the pool slot order keeps
+  // each aligned run of 4 slots contiguous, so every dim of the chunk is one
+  // 8-byte write of 4 slots into its V^T row (with the chunk swizzle).  Keys
+  // past nk become zeros.  (Here the conversion of tile j+1 overlaps other
+  // waves' products, so a few waves may carry all of V; attn_bf16_kernel
+  // converts between two barriers and keeps one item per thread and tile.)
   auto convert = [&](int stage, int b, int nk) {
     const uint8_t* st8 = lds8 + stage * STAGE8;
     uint16_t* tk = lds_t + b * 2 * TILE_ELEMS;
     int t0 = tid;
     asm volatile("" : "+v"(t0));
-    for (int it = t0; it < 2 * KT * 8; it += W * 64) {
-      const bool is_v = it >= KT * 8;
-      const int r = (it >> 3) & (KT - 1), ch = it & 7;  // token, 8-dim chunk
-      const uint2 w = *reinterpret_cast<const uint2*>(st8 + (is_v ? 4096 : 0) + r * D + ch * 8);
-      const int e = static_cast<int8_t>(st8[8192 + (is_v ? KT : 0) + r]);
+    // 8 codes of token r, dims 8ch..8ch+7, as 4 words of two bf16 each
+    auto dequant = [&](int off, int r, int ch, uint32_t (&u)[4]) {
+      const uint2 w = *reinterpret_cast<const uint2*>(st8 + off + r * D + ch * 8);
+      const int e = static_cast<int8_t>(st8[8192 + (off ? KT : 0) + r]);
       const float sc = __builtin_ldexpf(1.f, e);
       bf16x2 v2[4];
       v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, false);
       v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, true);
       v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, false);
       v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, true);
-      uint32_t u[4];
       __builtin_memcpy(u, v2, sizeof u);
       if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
-      if (!is_v) {
+    };
+    for (int it = t0; it < KT * 8 + KT * 2; it += W * 64) {
+      if (it < KT * 8) {
+        const int r = it >> 3, ch = it & 7;
+        uint32_t u[4];
+        dequant(0, r, ch, u);
         *reinterpret_cast<uint4*>(tk + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
       } else {
-        const int pos = v_slot_pos(r);
+        const int q = it - KT * 8;
+        const int r0 = (q >> 3) * 4, ch = q & 7;  // tokens r0..r0+3
+        uint32_t u0[4], u1[4], u2[4], u3[4];
+        dequant(4096, r0, ch, u0);
+        dequant(4096, r0 + 1, ch, u1);
+        dequant(4096, r0 + 2, ch, u2);
+        dequant(4096, r0 + 3, ch, u3);
+        const int pos = v_slot_pos(r0);  // slots r0..r0+3 sit at pos..pos+3
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int row = ch * 8 + jj;  // dim
-          tk[TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
-              static_cast<uint16_t>(u[jj >> 1] >> (16 * (jj & 1)));
+          const int sh = 16 * (jj & 1);
+          const uint32_t lo = ((u0[jj >> 1] >> sh) & 0xFFFFu) | (((u1[jj >> 1] >> sh) & 0xFFFFu) << 16);
+          const uint32_t hi = ((u2[jj >> 1] >> sh) & 0xFFFFu) | (((u3[jj >> 1] >> sh) & 0xFFFFu) << 16);
+          *reinterpret_cast<uint2*>(tk + TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))) =
+              make_uint2(lo, hi);
         }
       }
     }
