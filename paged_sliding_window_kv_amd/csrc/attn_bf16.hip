@@ -390,8 +390,10 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
     }
   };
   // KV8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`:
-  // K rows keep their layout; V rows become V^T rows (dims) in the pool slot
-  // order v_slot_pos with the chunk swizzle.  Keys past nk become zeros.
+  // K items (token, 8-dim chunk) become 16-byte row writes; V items (4
+  // consecutive tokens, 2 dims) become one 8-byte write of 4 slots per dim
+  // into its V^T row (the pool slot order keeps aligned runs of 4 slots
+  // contiguous), with the chunk swizzle.  Keys past nk become zeros.
   auto convert = [&](int stage, int b, int nk) {
     const uint8_t* st8 = lds8 + stage * STAGE8;
     uint16_t* tk = lds_t + b * 2 * TILE_ELEMS;
@@ -400,30 +402,44 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
     // would hold registers the products need.
     int t0 = tid;
     asm volatile("" : "+v"(t0));
+    typedef __bf16 bf16x2_ __attribute__((__vector_size__(2 * sizeof(__bf16))));
     for (int it = t0; it < 2 * KT * 8; it += W * 64) {
-      const bool is_v = it >= KT * 8;
-      const int r = (it >> 3) & (KT - 1), ch = it & 7;  // token, 8-dim chunk
-      const uint2 w = *reinterpret_cast<const uint2*>(st8 + (is_v ? 4096 : 0) + r * D + ch * 8);
-      const int e = static_cast<int8_t>(st8[8192 + (is_v ? KT : 0) + r]);
-      const float sc = __builtin_ldexpf(1.f, e);
-      typedef __bf16 bf16x2_ __attribute__((__vector_size__(2 * sizeof(__bf16))));
-      bf16x2_ v2[4];
-      v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, false);
-      v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, true);
-      v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, false);
-      v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, true);
-      uint32_t u[4];
-      __builtin_memcpy(u, v2, sizeof u);
-      if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
-      if (!is_v) {
+      if (it < KT * 8) {
+        const int r = it >> 3, ch = it & 7;  // token, 8-dim chunk
+        const uint2 w = *reinterpret_cast<const uint2*>(st8 + r * D + ch * 8);
+        const int e = static_cast<int8_t>(st8[8192 + r]);
+        const float sc = __builtin_ldexpf(1.f, e);
+        bf16x2_ v2[4];
+        v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, false);
+        v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.x), sc, true);
+        v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, false);
+        v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w.y), sc, true);
+        uint32_t u[4];
+        __builtin_memcpy(u, v2, sizeof u);
+        if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
         *reinterpret_cast<uint4*>(tk + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
       } else {
-        const int pos = v_slot_pos(r);
+        const int q = it - KT * 8;
+        const int r0 = (q >> 5) * 4, d0 = (q & 31) * 2;  // tokens r0..r0+3, dims d0, d0+1
+        uint32_t v[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = ch * 8 + j;  // dim
-          tk[TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))] =
-              static_cast<uint16_t>(u[j >> 1] >> (16 * (j & 1)));
+        for (int t = 0; t < 4; ++t) {
+          const int r = r0 + t;
+          const int w = *reinterpret_cast<const uint16_t*>(st8 + 4096 + r * D + d0);
+          const int e = static_cast<int8_t>(st8[8192 + KT + r]);
+          const bf16x2_ c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, __builtin_ldexpf(1.f, e), false);
+          __builtin_memcpy(&v[t], &c2, 4);
+          if (r >= nk) v[t] = 0u;
+        }
+        const int pos = v_slot_pos(r0);  // slots r0..r0+3 sit at pos..pos+3
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = d0 + i;  // dim
+          const int sh = 16 * i;
+          const uint32_t lo = ((v[0] >> sh) & 0xFFFFu) | (((v[1] >> sh) & 0xFFFFu) << 16);
+          const uint32_t hi = ((v[2] >> sh) & 0xFFFFu) | (((v[3] >> sh) & 0xFFFFu) << 16);
+          *reinterpret_cast<uint2*>(tk + TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))) =
+              make_uint2(lo, hi);
         }
       }
     }
@@ -1406,13 +1422,11 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
     }
   };
   // FP8: converts staged tile `stage` (nk valid keys) into bf16 buffer `b`.
-  // K: one thread per (token, 8-dim chunk), a 16-byte row write.  V: one
-  // thread per (4 consecutive tokens, 8-dim chunk); the pool slot order keeps
-  // each aligned run of 4 slots contiguous, so every dim of the chunk is one
-  // 8-byte write of 4 slots into its V^T row (with the chunk swizzle).  Keys
-  // past nk become zeros.  (Here the conversion of tile j+1 overlaps other
-  // waves' products, so a few waves may carry all of V; attn_bf16_kernel
-  // converts between two barriers and keeps one item per thread and tile.)
+  // Each thread takes one K item, a (token, 8-dim chunk) converted into one
+  // 16-byte row write, and one V item, 4 consecutive tokens x 2 dims: the
+  // pool slot order keeps each aligned run of 4 slots contiguous, so each of
+  // the 2 dims is one 8-byte write of 4 slots into its V^T row (with the chunk
+  // swizzle).  Every thread does the same work.  Keys past nk become zeros.
   auto convert = [&](int stage, int b, int nk) {
     const uint8_t* st8 = lds8 + stage * STAGE8;
     uint16_t* tk = lds_t + b * 2 * TILE_ELEMS;
@@ -1431,27 +1445,33 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
       __builtin_memcpy(u, v2, sizeof u);
       if (r >= nk) u[0] = u[1] = u[2] = u[3] = 0u;
     };
-    for (int it = t0; it < KT * 8 + KT * 2; it += W * 64) {
-      if (it < KT * 8) {
+    for (int it = t0; it < KT * 8; it += W * 64) {
+      {
         const int r = it >> 3, ch = it & 7;
         uint32_t u[4];
         dequant(0, r, ch, u);
         *reinterpret_cast<uint4*>(tk + r * D + ((ch ^ swz(r)) << 3)) = make_uint4(u[0], u[1], u[2], u[3]);
-      } else {
-        const int q = it - KT * 8;
-        const int r0 = (q >> 3) * 4, ch = q & 7;  // tokens r0..r0+3
-        uint32_t u0[4], u1[4], u2[4], u3[4];
-        dequant(4096, r0, ch, u0);
-        dequant(4096, r0 + 1, ch, u1);
-        dequant(4096, r0 + 2, ch, u2);
-        dequant(4096, r0 + 3, ch, u3);
+      }
+      {
+        // V: tokens r0..r0+3, dims d0, d0+1 (a quarter of an 8-dim chunk)
+        const int r0 = (it >> 5) * 4, d0 = (it & 31) * 2;
+        uint32_t v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = r0 + t;
+          const int w = *reinterpret_cast<const uint16_t*>(st8 + 4096 + r * D + d0);
+          const int e = static_cast<int8_t>(st8[8192 + KT + r]);
+          const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, __builtin_ldexpf(1.f, e), false);
+          __builtin_memcpy(&v[t], &c2, 4);
+          if (r >= nk) v[t] = 0u;
+        }
         const int pos = v_slot_pos(r0);  // slots r0..r0+3 sit at pos..pos+3
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int row = ch * 8 + jj;  // dim
-          const int sh = 16 * (jj & 1);
-          const uint32_t lo = ((u0[jj >> 1] >> sh) & 0xFFFFu) | (((u1[jj >> 1] >> sh) & 0xFFFFu) << 16);
-          const uint32_t hi = ((u2[jj >> 1] >> sh) & 0xFFFFu) | (((u3[jj >> 1] >> sh) & 0xFFFFu) << 16);
+        for (int i = 0; i < 2; ++i) {
+          const int row = d0 + i;  // dim
+          const int sh = 16 * i;
+          const uint32_t lo = ((v[0] >> sh) & 0xFFFFu) | (((v[1] >> sh) & 0xFFFFu) << 16);
+          const uint32_t hi = ((v[2] >> sh) & 0xFFFFu) | (((v[3] >> sh) & 0xFFFFu) << 16);
           *reinterpret_cast<uint2*>(tk + TILE_ELEMS + row * D + ((((pos >> 3) ^ swz(row)) << 3) | (pos & 7))) =
               make_uint2(lo, hi);
         }
