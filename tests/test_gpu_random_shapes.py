@@ -67,3 +67,55 @@ def test_random_batches_against_oracle(dtype, case):
         check_attention(o[a:b], lse[a:b], ro, rl, dtype, f"{dtype} case {case} seq={s_} q={b - a} Lk={gk.shape[1]}")
         if not sel:
             assert (to_f64(o[a:b]) == 0).all()
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_fp8_batches_against_oracle(case):
+    """The same random batches over FP8 pages: E4M3 codes and per-(token, head) row
+    exponents from the oracle's quantiser ("vLLM-Omni RFC #2727", section 3.4), stale
+    slots past each page's length holding NaN codes (0xFF) with exponent 127.  The
+    oracle attends in fp64 over the dequantised keys and values."""
+    import torch
+    from oracle import dequantize_rows, quantize_rows
+    from paged_sliding_window_kv_amd import paged_attention
+    rng = np.random.default_rng(9200 + case)
+    H = int(rng.integers(1, 4))
+    P, N = 256, 48
+    nseq = int(rng.integers(1, 4))
+    qlens = [int(rng.choice(_QN)) for _ in range(nseq)]
+    counts = [int(rng.integers(0, 6)) for _ in range(nseq)]
+    if sum(counts) == 0:
+        counts[0] = 1
+    ids = rng.choice(N, size=sum(counts), replace=False).astype(np.int32)
+    lens = rng.integers(1, P + 1, size=sum(counts)).astype(np.int32)
+    lens[rng.random(sum(counts)) < 0.5] = P
+    kv = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    splits = int(rng.choice([0, 0, 1, 2, 3, 7]))
+    log(f"fp8 case {case}: H={H} qlens={qlens} pages={counts} splits={splits}")
+    kc, ke = quantize_rows(bits_f64(synth.normal_tokens(12, case, 0, 1, N * H * P, 1, 64, "bf16")).reshape(N, H, P, 64))
+    vc, ve = quantize_rows(bits_f64(synth.normal_tokens(12, case, 0, 2, N * H * P, 1, 64, "bf16")).reshape(N, H, P, 64))
+    for p_, n in zip(ids, lens):
+        kc[p_, :, n:] = 0xFF
+        vc[p_, :, n:] = 0xFF
+        ke[p_, :, n:] = 127
+        ve[p_, :, n:] = 127
+    # flat pool buffers: codes [N][H][P][d], then exponents [N][H][P]
+    kbuf = torch.from_numpy(np.concatenate([kc.reshape(-1), ke.view(np.uint8).reshape(-1)])).cuda()
+    vbuf = torch.from_numpy(np.concatenate([vc.reshape(-1), ve.view(np.uint8).reshape(-1)])).cuda()
+    q = synth.normal_tokens(12, case, 0, 0, int(qo[-1]), H, 64, "bf16")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    o, lse = paged_attention(to_dev(q, "bf16"), kbuf, vbuf, dev(ids), dev(lens), dev(qo), dev(kv),
+                             max_qo_len=max(qlens), max_kv_pages=max(counts), num_splits=splits, fp8_pages=(N, P))
+    for s_ in range(nseq):
+        a, b = qo[s_], qo[s_ + 1]
+        sel = list(zip(ids[kv[s_]:kv[s_ + 1]], lens[kv[s_]:kv[s_ + 1]]))
+        if sel:
+            gk = np.concatenate([dequantize_rows(kc[p_, :, :n], ke[p_, :, :n]) for p_, n in sel], axis=1)
+            gv = np.concatenate([dequantize_rows(vc[p_, :, :n], ve[p_, :, :n]) for p_, n in sel], axis=1)
+        else:
+            gk = gv = np.zeros((H, 0, 64))
+        ro, rl = attention_f64(bits_f64(q[a:b]), gk, gv)
+        check_attention(o[a:b], lse[a:b], ro, rl, "bf16", f"fp8 case {case} seq={s_} q={b - a} Lk={gk.shape[1]}")
+        if not sel:
+            assert (to_f64(o[a:b]) == 0).all()
