@@ -555,11 +555,18 @@ def run_global(args) -> dict:
 
     one_pass()
     torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)  # inputs, pools, outputs, workspace: all resident
+    torch.cuda.reset_peak_memory_stats(dev)
     t0 = time.perf_counter()
     for _ in range(steps):
         one_pass()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    peak = torch.cuda.max_memory_allocated(dev)
+    # the score matrix one layer's head would need if it were stored (bf16)
+    score_bytes = T * T * 2
+    log(f"[bench] global: device memory {base / 2**30:.2f} GiB before the pass, peak {peak / 2**30:.2f} GiB during it "
+        f"(one head's {T} x {T} bf16 score matrix alone would be {score_bytes / 2**30:.1f} GiB)")
     fl_g = L * attn_flops(T, T, H)
     fl_f = L * frames * attn_flops(VGGT_TOKENS, VGGT_TOKENS, H)
     tf = steps * (fl_g + fl_f) / el / 1e12
@@ -577,7 +584,9 @@ def run_global(args) -> dict:
         "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
         "config": {"workload": f"vggt_global: 24 layers, 100 frames x 1374 tokens = {T}, 16 heads x 64, bf16, "
                                "global attention (no mask) + per-frame attention per layer, appends included",
-                   "layers": L, "heads": H, "head_dim": 64, "tokens": T},
+                   "layers": L, "heads": H, "head_dim": 64, "tokens": T,
+                   "device_memory_gib": base / 2**30, "peak_device_memory_gib": peak / 2**30,
+                   "score_matrix_one_head_gib": score_bytes / 2**30},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": "global attention call (attn_wide_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
