@@ -234,7 +234,8 @@ int paged_attn_fwd(const paged_attn_args* args, kvc_stream_t stream);
  * lse = log sum_i exp(lse_i).  partial_o: device fp32 [num_parts][rows][H][d],
  * partial_lse: device fp32 [num_parts][rows][H]; o in `dtype`, lse nullable.
  * Exposed for testing the merge on its own; paged_attn_fwd calls it when it
- * splits. */
+ * splits.  partial_o and o must be 16-byte aligned (KVC_ERR_INVALID_ARGUMENT
+ * otherwise). */
 int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
                      const float* partial_o, const float* partial_lse, void* o, float* lse,
                      kvc_stream_t stream);

@@ -648,6 +648,9 @@ int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num
   if (num_parts <= 0 || rows < 0 || num_heads <= 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad sizes");
   if (rows == 0) return KVC_OK;
   if (!partial_o || !partial_lse || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL pointer");
+  // the merge reads partial O and writes O in 16- and 8-byte vectors
+  if ((reinterpret_cast<uintptr_t>(partial_o) & 15) || (reinterpret_cast<uintptr_t>(o) & 15))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "partial_o and o must be 16-byte aligned");
   const hipError_t e = kvc::launch_attn_merge(dtype, num_parts, rows, num_heads, partial_o, partial_lse, o, lse,
                                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));

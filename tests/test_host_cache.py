@@ -165,6 +165,10 @@ def test_error_paths():
         assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == L.KVC_ERR_INVALID_ARGUMENT, field
         setattr(a, field, C.c_void_p(4096))
         assert lib.paged_attn_workspace_size(C.byref(a), C.byref(sz)) == 0, field
+    # the public merge checks its vectors' alignment before launching anything
+    f32 = C.c_void_p(4096 + 4)
+    assert lib.paged_attn_merge(L.KVC_DTYPE_F32, 2, 4, 1, 64, f32, C.c_void_p(4096), C.c_void_p(4096), None,
+                                None) == L.KVC_ERR_INVALID_ARGUMENT
 
 
 def test_split_choice_and_workspace():
