@@ -602,6 +602,12 @@ def keyframe_kept(t: int, c=KEYFRAME) -> bool:
     return t < c["scale"] or (t - c["scale"]) % c["interval"] == 0
 
 
+def keyframe_lk(units: int, c=KEYFRAME) -> int:
+    """Visible tokens with `units` units in the cache: scale + window patches, and the
+    special tokens of every unit (special pages are never evicted)."""
+    return (min(units, c["scale"]) + min(max(units - c["scale"], 0), c["window"])) * c["patch"] + units * c["special"]
+
+
 def run_keyframe(args) -> dict:
     """Keyframe stream: 1 layer, 4 heads x 64, fp32 pages, 2 scale + 4 window frames, keyframe interval 4.
 
@@ -662,8 +668,7 @@ def run_keyframe(args) -> dict:
     # visible tokens when frame t attends: its own unit plus the units kept before it
     total_flops, lks, kept = 0.0, [], 0
     for t in range(frames):
-        u = kept + 1
-        lk = (min(u, c["scale"]) + min(max(u - c["scale"], 0), c["window"])) * c["patch"] + u * c["special"]
+        lk = keyframe_lk(kept + 1)
         lks.append(lk)
         total_flops += attn_flops(tok, lk, H, d)
         kept += keyframe_kept(t)
