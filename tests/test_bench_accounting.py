@@ -38,3 +38,22 @@ def test_keyframe_rule_and_visible_tokens_match_oracle():
         else:
             oc.rollback()
         assert _visible(oc) == (bench.keyframe_lk(kept) if kept else 0), t
+
+
+def test_chunked_and_global_visible_tokens_match_oracle():
+    """Chunked: after the window fills, a chunk attends to window_chunks x chunk tokens.
+    Global (no window): after 100 frames all 137,400 tokens are visible."""
+    tokens = bench.CHUNK["frames_per_chunk"] * bench.VGGT_TOKENS
+    W = bench.CHUNK["window_chunks"]
+    oc = OracleCache(OracleConfig(num_heads=1, head_dim=64, page_size=bench.CHUNK["page"], patch_tokens=tokens,
+                                  special_tokens=0, num_scale_units=0, window_units=W, max_units=W + 3),
+                     with_pool=False)
+    for i in range(W + 3):
+        oc.append()
+        assert _visible(oc) == min(i + 1, W) * tokens
+    og = OracleCache(OracleConfig(num_heads=1, head_dim=64, page_size=256, patch_tokens=bench.VGGT_TOKENS,
+                                  special_tokens=0, num_scale_units=0, window_units=0, max_units=100),
+                     with_pool=False)
+    for _ in range(100):
+        og.append()
+    assert _visible(og) == 100 * bench.VGGT_TOKENS == 137400
