@@ -257,7 +257,9 @@ def run_stream(args) -> dict:
     if args.warmup:
         b.run(args.warmup)
         torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(b.dev)  # pools, inputs, outputs, workspace
     elapsed = b.timed(frames)
+    mem_growth = torch.cuda.memory_allocated(b.dev) - mem0
     lk_sum, npages = b.check_tables()
     assert lk_sum == stream_lk(frames - 1), (lk_sum, stream_lk(frames - 1))
     total_flops = sum(layers * attn_flops(b.tokens, stream_lk(t), STREAM["heads"]) for t in range(frames))
@@ -283,6 +285,7 @@ def run_stream(args) -> dict:
             "layers": layers, "heads": 16, "head_dim": 64, "page_size": 256, "frames": frames,
             "final_visible_tokens": lk_sum, "final_visible_pages": npages, "kv_dtype": args.kv_dtype,
             "kv_pool_mib_per_layer": (b.caches[0].k_pool.numel() * b.caches[0].k_pool.element_size() * 2) / 2**20,
+            "device_memory_growth_bytes": mem_growth,
         },
         "roofline": {
             "bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
