@@ -101,6 +101,24 @@ def test_fp8_peaky_queries():
     check_attention(o, lse, ro, rl, "bf16", f"peaky Lk={gk.shape[1]}")
 
 
+def test_fp8_peaky_queries_large_tiles():
+    """Large scores (q scaled by 4) with chunk units of 2 x 1374 tokens: FP8 pages on the
+    512-row tiles, through the running-maximum rescale path, with and without splits."""
+    import torch
+    H, P = 2, 2 * 1374
+    oc, dc = _caches(H, P, 0, 0, 3, FRAME_ALIGNED, 5)
+    for t in range(5):
+        q, k, v = synth.frame_qkv(14, 0, t, P, H, 64, "bf16", q_scale=4.0)
+        oc.append(k, v)
+        dc.append(to_dev(k, "bf16"), to_dev(v, "bf16"))
+    gk, gv = oc.gather()
+    ro, rl = attention_f64(bits_f64(q), gk, gv)
+    for ns in (0, 1, 4):
+        o, lse = dc.attend(to_dev(q, "bf16"), num_splits=ns)
+        torch.cuda.synchronize()
+        check_attention(o, lse, ro, rl, "bf16", f"peaky chunks splits={ns or 'auto'} Lk={gk.shape[1]}")
+
+
 def test_fp8_lingbot_stream_1000_frames():
     """The 1000-frame LingBot-shaped stream with FP8 pages: last step (24,432 keys) against the oracle."""
     import torch
