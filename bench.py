@@ -1,29 +1,41 @@
 #!/usr/bin/env python3
 """Throughput of paged sliding-window KV attention on one MI355X.
 
-Default workload (one JSON line on stdout): a LingBot-Map-shaped stream.
-24 independent layer caches, 16 heads x 64 dims, bf16.  Each frame carries
-256 patch and 6 special tokens.  There are 8 scale frames, a 64-frame window
-and 42 frames per special page.  1000 frames are streamed.  One step is one
-frame through all 24 layers: the append (scatter of K/V into pages), the
-visible table and the attention of the frame's 262 query tokens against it.
-Inputs are seeded synthetic N(0,1) tensors, resident in HBM before timing.
+Default workload (one JSON line on stdout): VGGT-style chunked global
+attention ("vLLM-Omni RFC #2727: Reconstruction Engine", sections 1, 2.2 and
+2.3).  24 layer caches, 16 heads x 64 dims, bf16; a unit is a chunk of 8
+frames x 1374 tokens = 10,992 query tokens (43 pages of 256), and the window
+keeps the last 4 chunks including the current one, so every timed chunk
+attends to 43,968 keys.  One step is one chunk through all 24 layers: the
+append (scatter of the chunk's K/V into pages) and the attention of its
+10,992 queries against the visible table.  `--steps K` times K such steps
+after at least 4 untimed ones (the window full); it never changes the
+shapes.  Inputs are seeded synthetic N(0,1) tensors, resident in HBM before
+timing.
 
-Other workloads (--workload): "chunked" is VGGT-style chunked global attention
-(8-frame chunks of 1374 tokens, window of 4 chunks).  "global" is full global
-attention over 100 frames x 1374 tokens followed by per-frame attention.
-"stream_batched" runs --batch LingBot streams side by side: per layer and frame,
-each stream appends its frame and one launch serves all streams' attention.
-"keyframe" is a small fp32 stream over 10,000 frames that keeps every fourth
-frame and rolls the others back; it reports frames/s and checks that device
-memory and the patch-page count stay constant.
+The line also carries, at full size, the LingBot-Map-shaped stream
+("LingBot-Map Paged KV Cache", sections 1-2): 24 layer caches, 1,000 frames
+of 256 patch + 6 special tokens, 8 scale frames, a 64-frame window, special
+pages of 42 frames, each frame's 262 queries attending after its append.
+
+Other workloads (--workload): "stream" (the LingBot stream as the main line;
+--steps K times the last K of its 1,000 frames), "global" (full global
+attention over 100 frames x 1374 tokens, then per-frame attention),
+"stream_batched" (--batch LingBot streams, one attention launch per layer and
+frame), "keyframe" (a small fp32 stream over 10,000 frames that keeps every
+fourth frame and rolls the others back).
+
+Every workload reports `roofline` for its dominant kernel (algorithmic FLOPs
+or bytes per launch over the kernel's own duration, taken with HIP events on
+the launch stream: the library records an event right after the attention
+kernel and before the merge of split partials) and `cpu_baseline` (the
+oracle timed on the host on a bounded slice of the same workload).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes as C
 import json
-import math
 import os
 import sys
 import time
@@ -35,17 +47,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged attention TFLOP/s + streamed frames/s (% of bf16 MFMA peak), 1 MI355X"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix cores (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+VGGT_TOKENS = 1374
+CHUNK = dict(layers=24, heads=16, d=64, page=256, frames_per_chunk=8, window_chunks=4)
+STREAM = dict(layers=24, heads=16, d=64, page=256, patch=256, special=6, scale=8, window=64, frames=1000)
+KEYFRAME = dict(heads=4, d=64, page=256, patch=256, special=6, scale=2, window=4, interval=4, frames=10000)
+GLOBAL = dict(layers=24, heads=16, d=64, frames=100)
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-# ----------------------------------------------------------------------------
-# shared pieces
-# ----------------------------------------------------------------------------
 def _ok(status: int, where: str) -> None:
     if status != 0:
         from paged_sliding_window_kv_amd import _lib as L
@@ -83,17 +99,291 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def host_info() -> dict:
+    """Host cores, CPU model and the BLAS numpy runs on (the oracle's matrix products)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        pass
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads(), "cpu_model": model,
+            "blas": blas, "numpy": np.__version__}
+
+
+def cpu_baseline(value: float, unit: str, sample: str, sec: float, extra: dict | None = None) -> dict:
+    h = host_info()
+    out = {"value": value, "unit": unit, "cores": h["blas_threads"], "kind": "oracle", "sample": sample,
+           "seconds": sec, "host_cores": h["cores"], "cpu_model": h["cpu_model"], "blas": h["blas"],
+           "numpy": h["numpy"]}
+    if extra:
+        out.update(extra)
+    return out
+
+
+class CallClock:
+    """HIP events around attention calls on the launch stream.
+
+    For call i: `before(i)` records a start event and hands the library a
+    kernel-done event, which it records right after the attention kernel (and
+    before the merge of split partials); `after(i)` records an end event.
+    start -> kernel-done is the attention kernel alone, start -> end the call.
+    """
+
+    def __init__(self, n: int):
+        import torch
+        from paged_sliding_window_kv_amd import lib
+        self.torch, self.lib = torch, lib()
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for trio in self.ev:  # torch creates the HIP events at their first record
+            for e in trio:
+                e.record()
+        torch.cuda.synchronize()
+        self.kernel_s = 0.0
+        self.call_s = 0.0
+        self.calls = 0
+
+    def before(self, i: int) -> None:
+        self.ev[i][0].record()
+        _ok(self.lib.kvc_set_kernel_done_event(C.c_void_p(self.ev[i][1].cuda_event)), "kvc_set_kernel_done_event")
+
+    def after(self, i: int) -> None:
+        self.ev[i][2].record()
+        _ok(self.lib.kvc_set_kernel_done_event(None), "kvc_set_kernel_done_event")
+
+    def collect(self, n: int) -> None:
+        """Adds calls 0..n-1 (after a synchronize) to the totals."""
+        self.torch.cuda.synchronize()
+        for i in range(n):
+            s, k, e = self.ev[i]
+            self.kernel_s += s.elapsed_time(k) * 1e-3
+            self.call_s += s.elapsed_time(e) * 1e-3
+        self.calls += n
+
+
+def run_probes() -> dict:
+    """Measured denominators: dense bf16 matrix-core rate and HBM read/copy bandwidth (include/kvc_probe.h)."""
+    import torch
+    from paged_sliding_window_kv_amd import lib
+    lb = lib()
+    dev = torch.device("cuda:0")
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    scratch = torch.empty(lb.kvc_probe_scratch_bytes(), dtype=torch.uint8, device=dev)
+    tf = C.c_double()
+    _ok(lb.kvc_probe_mfma_bf16(scratch.data_ptr(), scratch.numel(), sp, C.byref(tf)), "kvc_probe_mfma_bf16")
+    nb = 2 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    rd, cp = C.c_double(), C.c_double()
+    _ok(lb.kvc_probe_hbm(src.data_ptr(), dst.data_ptr(), nb, scratch.data_ptr(), scratch.numel(), sp, C.byref(rd),
+                         C.byref(cp)), "kvc_probe_hbm")
+    del src, dst, scratch
+    torch.cuda.empty_cache()
+    out = {"mfma_bf16_tflops": tf.value, "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
+           "mfma_probe": "1,024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16 from registers",
+           "hbm_probe": "2 GiB streaming read (16-byte loads) and 2 GiB copy (read + write bytes)"}
+    log(f"[bench] probes: bf16 matrix cores {tf.value:.0f} TFLOP/s, HBM read {rd.value:.0f} GB/s, "
+        f"copy {cp.value:.0f} GB/s")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# VGGT-style chunked global attention (the default line)
+# ----------------------------------------------------------------------------
+def chunk_tokens() -> int:
+    return CHUNK["frames_per_chunk"] * VGGT_TOKENS
+
+
+def oracle_chunked_sample(query_rows: int = 1024, seed: int = 0):
+    """The oracle on a bounded slice of the chunked workload: one layer, all 16 heads.
+
+    Four chunks fill the window untimed.  Timed: the append of the fifth chunk
+    (the oldest is evicted), the gather of the 43,968 visible keys and the fp64
+    attention of that chunk's first `query_rows` queries.  Returns (seconds,
+    flops of the attention part, visible keys).
+    """
+    import synth
+    from oracle import OracleCache, OracleConfig, attention_f64, to_f64
+    c, T, W = CHUNK, chunk_tokens(), CHUNK["window_chunks"]
+    oc = OracleCache(OracleConfig(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], patch_tokens=T,
+                                  special_tokens=0, num_scale_units=0, window_units=W, max_units=W + 1,
+                                  store_dtype="bf16"))
+    bank = [synth.frame_qkv(seed, 0, i, T, c["heads"], c["d"], "bf16") for i in range(2)]
+    for i in range(W):
+        oc.append(bank[i % 2][1], bank[i % 2][2])
+    q, k, v = bank[W % 2]
+    t0 = time.perf_counter()
+    oc.append(k, v)
+    gk, gv = oc.gather()
+    attention_f64(to_f64(q[:query_rows]), to_f64(gk), to_f64(gv))
+    sec = time.perf_counter() - t0
+    return sec, attn_flops(query_rows, gk.shape[1], c["heads"], c["d"]), gk.shape[1]
+
+
+def run_chunked(args) -> dict:
+    """Chunks of 8 frames (10,992 tokens, 43 pages) attend to the last 4 chunks (43,968 keys)."""
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, lib
+    c = CHUNK
+    L, H, W, T = c["layers"], c["heads"], c["window_chunks"], chunk_tokens()
+    steps, warm = args.steps, max(args.warmup, W)
+    log(f"[bench] chunked: {L} layers, chunk {T} tokens, window {W} chunks, {warm} untimed and {steps} timed "
+        f"chunk steps, KV {args.kv_dtype}")
+    dev = torch.device("cuda:0")
+    lb = lib()
+    caches = [KvCache(num_heads=H, dtype=args.kv_dtype, patch_tokens=T, special_tokens=0, num_scale_units=0,
+                      window_units=W, max_units=warm + 2 * steps, device=dev) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    bank = 2
+    shp = (bank, T, H, c["d"])
+    qs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    ks = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    vs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+    out = torch.empty((T, H, c["d"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    wsb = max(cc.workspace_bytes(T) for cc in caches)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    kr = args.keep_ratio
+    clock = CallClock(L)
+
+    def step(i, timed_calls=False):
+        b = i % bank
+        for l in range(L):
+            _ok(lb.kvc_append_frame(caches[l].handle, ks[l][b].data_ptr(), vs[l][b].data_ptr(), sp), "append")
+            if timed_calls:
+                clock.before(l)
+            if kr < 1.0:
+                # AVGGT-style: each layer its own random page subset (seed = layer)
+                _ok(lb.kvc_attend_subset(caches[l].handle, kr, l, 0, 0, qs[l][b].data_ptr(), T, 0.0,
+                                         out.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend_subset")
+            else:
+                _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), T, 0.0, out.data_ptr(),
+                                  lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend")
+            if timed_calls:
+                clock.after(l)
+        if timed_calls:
+            clock.collect(L)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warm + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    lk = W * T
+    if kr < 1.0:
+        # keys each layer attends: the subset keeps the same table positions every steady-state step
+        lks = [int(caches[l].subset_table(kr, l)[1].sum()) for l in range(L)]
+    else:
+        lks = [lk] * L
+    flops_step = sum(attn_flops(T, x, H) for x in lks)
+    kv_e = kv_elem_bytes(args.kv_dtype)
+    bytes_call = sum(attn_bytes(T, x, H, kv_elem=kv_e) for x in lks) / L
+    # replay with events around every call (same shapes, full window)
+    for i in range(steps):
+        step(warm + steps + i, timed_calls=True)
+    n = clock.calls
+    flops_call = flops_step / L
+    k_us = clock.kernel_s / n * 1e6
+    c_us = clock.call_s / n * 1e6
+    ach = flops_call / (k_us * 1e-6) / 1e12
+    tf = steps * flops_step / el / 1e12
+    splits = caches[0].num_splits(T) if kr >= 1.0 else None
+    log(f"[bench] chunked: {el / steps * 1e3:.2f} ms/step, {tf:.1f} TFLOP/s, {steps * 8 / el:.1f} frames/s; "
+        f"attention kernel {k_us:.1f} us ({ach:.1f} TFLOP/s, {ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak), "
+        f"call with merge {c_us:.1f} us")
+    kernel = ("attn_wide_kernel" if args.kv_dtype == "bf16" else "attn_wide_kernel<FP8 pages>")
+    res = {
+        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3,
+        "frames_per_s": steps * c["frames_per_chunk"] / el,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+        "dtype": "bf16",
+        "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, {kv_label(args.kv_dtype)}, "
+                               f"chunks of 8 x 1374 = {T} query tokens (43 pages), window 4 chunks "
+                               f"({W * T} visible keys)"
+                               + (f", per-layer page subsets keeping {kr} ({sum(lks) / L:.0f} keys attended)"
+                                  if kr < 1.0 else "")
+                               + f"; step = one chunk through 24 layers (append + attention); {steps} timed steps "
+                               f"after {warm} untimed",
+                   "layers": L, "heads": H, "head_dim": 64, "chunk_tokens": T, "window_chunks": W,
+                   "visible_tokens": W * T, "keep_ratio": kr, "attended_tokens": sum(lks) / L,
+                   "kv_dtype": args.kv_dtype, "untimed_chunk_steps": warm, "key_splits": splits},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": kernel, "per_launch_flops": flops_call, "per_launch_bytes": bytes_call,
+                     "avg_kernel_us": k_us, "avg_call_us_with_merge": c_us, "calls": n,
+                     "call_tflops_with_merge": flops_call / (c_us * 1e-6) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows
+        log(f"[bench] oracle: 1 layer, 16 heads, {rows} of the chunk's {T} queries against {W * T} keys")
+        sec, fl, olk = oracle_chunked_sample(rows)
+        rate = fl / sec / 1e12
+        res["cpu_baseline"] = cpu_baseline(
+            rate, "TFLOP/s",
+            f"1 of 24 layers, all 16 heads, queries 0..{rows - 1} of a 10,992-query chunk against the {olk} "
+            f"visible keys (append of the chunk, gather of the window's pages, fp64 attention), {sec:.1f} s; "
+            f"extrapolated to a whole chunk step by the FLOP ratio",
+            sec, {"extrapolated": True, "frames_per_s": c["frames_per_chunk"] / (flops_step / (rate * 1e12)),
+                  "ms_per_step": flops_step / (rate * 1e12) * 1e3})
+        log(f"[bench] oracle: {rate * 1e3:.2f} GFLOP/s over {sec:.1f} s")
+    del caches, qs, ks, vs, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------
 # LingBot-Map-shaped stream
 # ----------------------------------------------------------------------------
-STREAM = dict(layers=24, heads=16, d=64, page=256, patch=256, special=6, scale=8, window=64, frames=1000)
-
-
 def stream_lk(t: int, c=STREAM) -> int:
     """Visible tokens after appending frame t (0-based): scale + window patches + all specials."""
     n = t + 1
     units = min(n, c["scale"]) + min(max(n - c["scale"], 0), c["window"])
     return units * c["patch"] + n * c["special"]
+
+
+def oracle_stream_sample(frames: int, sample: int, bank: int = 4, seed: int = 0):
+    """The oracle on a bounded sample of the LingBot stream: one layer.
+
+    Frames 0 .. frames - sample - 1 are appended untimed; the last `sample`
+    frames are timed (append, gather and fp64 attention of the frame's 262
+    queries).  The cache holds every frame's special tokens.  Returns
+    (seconds, flops of the timed attention, frames timed).
+    """
+    import synth
+    from oracle import OracleCache, OracleConfig, attention_f64, to_f64
+    c = STREAM
+    sample = max(1, min(sample, frames))
+    tok = c["patch"] + c["special"]
+    oc = OracleCache(OracleConfig(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], patch_tokens=c["patch"],
+                                  special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
+                                  max_units=frames, store_dtype="bf16"))
+    qkv = [synth.frame_qkv(seed, 0, i, tok, c["heads"], c["d"], "bf16") for i in range(bank)]
+    for t in range(frames - sample):
+        _, k, v = qkv[t % bank]
+        oc.append(k, v)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for t in range(frames - sample, frames):
+        q, k, v = qkv[t % bank]
+        oc.append(k, v)
+        gk, gv = oc.gather()
+        attention_f64(to_f64(q), to_f64(gk), to_f64(gv))
+        flops += attn_flops(tok, gk.shape[1], c["heads"], c["d"])
+    return time.perf_counter() - t0, flops, sample
 
 
 class StreamBench:
@@ -146,7 +436,7 @@ class StreamBench:
         for cc in self.caches:
             cc.reset()
 
-    def step(self, t: int):
+    def step(self, t: int, clock: CallClock | None = None):
         """One frame: per layer, append the frame's K/V, then attend (the stream's own order)."""
         lib, sp, b = self.lib, self.sp, t % self.bank
         app, att = lib.kvc_append_frame, lib.kvc_attend
@@ -155,160 +445,106 @@ class StreamBench:
             s = app(self.h[l], self.kp[l][b], self.vp[l][b], sp)
             if s:
                 _ok(s, "kvc_append_frame")
+            if clock is not None:
+                clock.before(l)
             s = att(self.h[l], self.qp[l][b], nq, 0.0, self.op[l], self.lp[l], wsp, wsb, sp)
             if s:
                 _ok(s, "kvc_attend")
-
-    def step_timed_attention(self, t: int, ev0, ev1):
-        """One frame with the 24 layers' attention calls back to back between two events.
-
-        The appends of the frame come first (each layer's call sees exactly the
-        cache it sees in the stream), so the events bracket attention calls
-        only, and their own cost is spread over 24 calls.
-        """
-        lib, sp, b = self.lib, self.sp, t % self.bank
-        app, att = lib.kvc_append_frame, lib.kvc_attend
-        wsp, wsb, nq = self.ws.data_ptr(), self.wsb, self.tokens
-        for l in range(self.layers):
-            s = app(self.h[l], self.kp[l][b], self.vp[l][b], sp)
-            if s:
-                _ok(s, "kvc_append_frame")
-        ev0.record(self.stream)
-        for l in range(self.layers):
-            s = att(self.h[l], self.qp[l][b], nq, 0.0, self.op[l], self.lp[l], wsp, wsb, sp)
-            if s:
-                _ok(s, "kvc_attend")
-        ev1.record(self.stream)
-
-    def run(self, frames: int):
-        for t in range(frames):
-            self.step(t)
-
-    def timed(self, frames: int) -> float:
-        torch = self.torch
-        self.reset()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        self.run(frames)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    def attention_kernel_time(self, frames: int):
-        """Replay the stream, timing each frame's attention calls with HIP events on the launch stream.
-
-        Returns (seconds inside attention calls, algorithmic bytes, flops) summed over the replay.
-        """
-        torch = self.torch
-        self.reset()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        tot = 0.0
-        byt = 0.0
-        flo = 0.0
-        c = self.c
-        for t in range(frames):
-            self.step_timed_attention(t, ev0, ev1)
-            ev1.synchronize()
-            tot += ev0.elapsed_time(ev1) * 1e-3
-            lk = stream_lk(t, c)
-            byt += self.layers * attn_bytes(self.tokens, lk, c["heads"], c["d"], kv_elem=self.kv_elem)
-            flo += self.layers * attn_flops(self.tokens, lk, c["heads"], c["d"])
-        return tot, byt, flo
+            if clock is not None:
+                clock.after(l)
+        if clock is not None:
+            clock.collect(self.layers)
 
     def check_tables(self):
         ids, lens = self.caches[0].visible_table()
         return int(lens.sum()), len(ids)
 
 
-def oracle_stream_sample(frames: int, sample: int, bank: int = 4, seed: int = 0):
-    """The CPU oracle on a bounded sample of the same stream: one layer.
-
-    Units are appended up to frame frames - sample - 1 untimed.  The last
-    `sample` frames are then timed: append, gather and fp64 attention.
-    Returns (seconds, flops of the timed part, frames timed).
-    """
-    import synth
-    from oracle import OracleCache, OracleConfig, attention_f64, to_f64
-    c = STREAM
-    tok = c["patch"] + c["special"]
-    oc = OracleCache(OracleConfig(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], patch_tokens=c["patch"],
-                                  special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
-                                  max_units=frames, store_dtype="bf16"))
-    qkv = [synth.frame_qkv(seed, 0, i, tok, c["heads"], c["d"], "bf16") for i in range(bank)]
-    for t in range(frames - sample):
-        _, k, v = qkv[t % bank]
-        oc.append(k, v)
-    flops = 0.0
-    t0 = time.perf_counter()
-    for t in range(frames - sample, frames):
-        q, k, v = qkv[t % bank]
-        oc.append(k, v)
-        gk, gv = oc.gather()
-        attention_f64(to_f64(q), to_f64(gk), to_f64(gv))
-        flops += attn_flops(tok, gk.shape[1], c["heads"], c["d"])
-    return time.perf_counter() - t0, flops, sample
-
-
-def run_stream(args) -> dict:
+def run_stream(args, timed: int | None = None, cpu_sample: int | None = None) -> dict:
+    """The 1,000-frame LingBot stream; the last `timed` frames are timed (all of them by default)."""
     import torch
-    frames, layers = args.steps, STREAM["layers"]
-    log(f"[bench] stream: {layers} layers x {frames} frames, warmup {args.warmup}")
-    b = StreamBench(max(frames, args.warmup), layers, kv_dtype=args.kv_dtype)
-    if args.warmup:
-        b.run(args.warmup)
-        torch.cuda.synchronize()
+    c = STREAM
+    frames, layers = c["frames"], c["layers"]
+    timed = frames if timed is None else max(1, min(timed, frames))
+    log(f"[bench] stream: {layers} layers x {frames} frames ({timed} timed), warmup {args.warmup}, "
+        f"KV {args.kv_dtype}")
+    b = StreamBench(frames, layers, kv_dtype=args.kv_dtype)
+    for t in range(args.warmup):
+        b.step(t)
+    torch.cuda.synchronize()
+    b.reset()
     mem0 = torch.cuda.memory_allocated(b.dev)  # pools, inputs, outputs, workspace
-    elapsed = b.timed(frames)
+    for t in range(frames - timed):
+        b.step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(frames - timed, frames):
+        b.step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     mem_growth = torch.cuda.memory_allocated(b.dev) - mem0
     lk_sum, npages = b.check_tables()
     assert lk_sum == stream_lk(frames - 1), (lk_sum, stream_lk(frames - 1))
-    total_flops = sum(layers * attn_flops(b.tokens, stream_lk(t), STREAM["heads"]) for t in range(frames))
+    heads = c["heads"]
+    total_flops = sum(layers * attn_flops(b.tokens, stream_lk(t), heads) for t in range(frames - timed, frames))
     tflops = total_flops / elapsed / 1e12
-    fps = frames / elapsed
-    log(f"[bench] timed {frames} frames in {elapsed:.3f} s: {tflops:.1f} TFLOP/s, {fps:.1f} frames/s")
-    att_s, att_b, att_f = b.attention_kernel_time(frames)
-    n_launch = frames * layers
-    avg_us = att_s / n_launch * 1e6
-    ach_gbs = att_b / att_s / 1e9
-    log(f"[bench] attention calls: {avg_us:.2f} us avg, {ach_gbs:.0f} GB/s, {att_f / att_s / 1e12:.1f} TFLOP/s")
+    fps = timed / elapsed
+    log(f"[bench] stream: timed {timed} frames in {elapsed:.3f} s: {tflops:.1f} TFLOP/s, {fps:.1f} frames/s")
+    # replay the whole stream with events around every attention call
+    b.reset()
+    clock = CallClock(layers)
+    byt = flo = 0.0
+    for t in range(frames):
+        b.step(t, clock)
+        lk = stream_lk(t)
+        byt += layers * attn_bytes(b.tokens, lk, heads, kv_elem=b.kv_elem)
+        flo += layers * attn_flops(b.tokens, lk, heads)
+    n = clock.calls
+    k_us, c_us = clock.kernel_s / n * 1e6, clock.call_s / n * 1e6
+    ach_gbs = byt / clock.kernel_s / 1e9
+    log(f"[bench] stream attention: kernel {k_us:.2f} us avg ({ach_gbs:.0f} GB/s, "
+        f"{flo / clock.kernel_s / 1e12:.1f} TFLOP/s), call with merge {c_us:.2f} us")
     res = {
         "value": tflops,
         "unit": "TFLOP/s",
-        "ms_per_step": elapsed / frames * 1e3,
+        "ms_per_step": elapsed / timed * 1e3,
         "frames_per_s": fps,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "dtype": "bf16",
         "config": {
             "workload": f"lingbot_stream: 24 layer caches, 16 heads x 64, {kv_label(args.kv_dtype)}, "
-                        "256 patch + 6 special tokens/frame, "
-                        "8 scale frames, 64-frame window, 42 frames/special page, 262 queries/step, "
-                        f"{frames} frames",
-            "layers": layers, "heads": 16, "head_dim": 64, "page_size": 256, "frames": frames,
-            "final_visible_tokens": lk_sum, "final_visible_pages": npages, "kv_dtype": args.kv_dtype,
+                        "256 patch + 6 special tokens/frame, 8 scale frames, 64-frame window, 42 frames/special "
+                        f"page, 262 queries/step, {frames} frames streamed, the last {timed} timed; step = one "
+                        "frame through 24 layers (append + attention)",
+            "layers": layers, "heads": heads, "head_dim": 64, "page_size": 256, "frames": frames,
+            "timed_frames": timed, "final_visible_tokens": lk_sum, "final_visible_pages": npages,
+            "kv_dtype": args.kv_dtype,
             "kv_pool_mib_per_layer": (b.caches[0].k_pool.numel() * b.caches[0].k_pool.element_size() * 2) / 2**20,
             "device_memory_growth_bytes": mem_growth,
         },
         "roofline": {
             "bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": ach_gbs / PEAK_HBM_GBS, "traffic": None,
-            "kernel": "paged attention call (attn_bf16_kernel + attn_merge16_kernel)",
-            "avg_call_us": avg_us, "calls": n_launch,
-            "bytes_per_call_avg": att_b / n_launch,
-            "attn_tflops": att_f / att_s / 1e12,
-            "attn_frac_bf16_peak": att_f / att_s / 1e12 / PEAK_BF16_TFLOPS,
+            "kernel": "attn_bf16_kernel (272-row tile)" if args.kv_dtype == "bf16" else "attn_bf16_kernel<FP8 pages>",
+            "per_launch_bytes": byt / n, "per_launch_flops": flo / n,
+            "avg_kernel_us": k_us, "avg_call_us_with_merge": c_us, "calls": n,
+            "kernel_tflops": flo / clock.kernel_s / 1e12,
+            "call_gbs_with_merge": byt / clock.call_s / 1e9,
         },
     }
-    if not args.no_cpu_baseline:
-        sample = args.cpu_sample
-        log(f"[bench] oracle sample: 1 layer, last {sample} of {frames} frames")
+    sample = args.cpu_sample if cpu_sample is None else cpu_sample
+    if not args.no_cpu_baseline and sample > 0:
+        log(f"[bench] oracle sample: 1 layer, the last {sample} of {frames} frames")
         sec, fl, nfr = oracle_stream_sample(frames, sample)
         ot = fl / sec / 1e12
-        res["cpu_baseline"] = {
-            "value": ot, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"1 of 24 layers, frames {frames - sample}..{frames - 1} of the {frames}-frame stream "
-                      f"(append + gather + fp64 attention), {sec:.1f} s",
-            "frames_per_s": 1.0 / (sec / nfr * layers),
-        }
+        res["cpu_baseline"] = cpu_baseline(
+            ot, "TFLOP/s",
+            f"1 of 24 layers, frames {frames - nfr}..{frames - 1} of the {frames}-frame stream "
+            f"(append + gather + fp64 attention), {sec:.1f} s; frames/s scaled to 24 layers",
+            sec, {"frames_per_s": 1.0 / (sec / nfr * layers)})
         log(f"[bench] oracle: {ot * 1e3:.2f} GFLOP/s over {sec:.1f} s")
+    del b
+    torch.cuda.empty_cache()
     return res
 
 
@@ -317,9 +553,10 @@ def run_stream_batched(args) -> dict:
     import torch
     from paged_sliding_window_kv_amd import attend_batch_workspace_bytes, lib, shared_pool_caches
     c = STREAM
-    B, L, frames = args.batch, c["layers"], args.steps
+    B, L, frames = args.batch, c["layers"], c["frames"]
+    timed = max(1, min(args.steps, frames))
     tok = c["patch"] + c["special"]
-    log(f"[bench] stream_batched: {B} streams x {L} layers x {frames} frames, warmup {args.warmup}")
+    log(f"[bench] stream_batched: {B} streams x {L} layers x {frames} frames ({timed} timed), warmup {args.warmup}")
     dev = torch.device("cuda:0")
     lb = lib()
     kw = dict(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"], dtype="bf16", patch_tokens=c["patch"],
@@ -339,10 +576,10 @@ def run_stream_batched(args) -> dict:
     qop = qo.ctypes.data_as(C.POINTER(C.c_int32))
     # largest workspace over the stream: the batch at its longest tables
     probe = shared_pool_caches(B, dev, **kw)
-    for _ in range(min(frames, c["scale"] + c["window"] + 1)):
+    for _ in range(frames):
         for cc in probe:
             cc.append(ks[0][0, :tok], vs[0][0, :tok])
-    wsb = attend_batch_workspace_bytes(probe, qo) * 2
+    wsb = attend_batch_workspace_bytes(probe, qo)
     del probe
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
@@ -350,19 +587,20 @@ def run_stream_batched(args) -> dict:
     handles = [(C.c_void_p * B)(*[cc.handle.value for cc in layer]) for layer in layers]
     hlist = [[cc.handle for cc in layer] for layer in layers]
 
-    def step(t, ev=None):
+    def step(t, clock=None):
         b = t % bank
         for l in range(L):
             kb, vb = ks[l].data_ptr() + b * B * fb, vs[l].data_ptr() + b * B * fb
             for i in range(B):
                 _ok(lb.kvc_append_frame(hlist[l][i], kb + i * fb, vb + i * fb, sp), "append")
-        if ev is not None:
-            ev[0].record()
-        for l in range(L):
+            if clock is not None:
+                clock.before(l)
             _ok(lb.kvc_attend_batch(handles[l], B, qs[l].data_ptr() + b * B * fb, qop, 0.0, out.data_ptr(),
                                     lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend_batch")
-        if ev is not None:
-            ev[1].record()
+            if clock is not None:
+                clock.after(l)
+        if clock is not None:
+            clock.collect(L)
 
     def reset():
         for layer in layers:
@@ -373,144 +611,87 @@ def run_stream_batched(args) -> dict:
         step(t)
     torch.cuda.synchronize()
     reset()
+    for t in range(frames - timed):
+        step(t)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for t in range(frames):
+    for t in range(frames - timed, frames):
         step(t)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    flops = sum(B * L * attn_flops(tok, stream_lk(t), c["heads"]) for t in range(frames))
-    byts = sum(B * L * attn_bytes(tok, stream_lk(t), c["heads"]) for t in range(frames))
+    flops = sum(B * L * attn_flops(tok, stream_lk(t), c["heads"]) for t in range(frames - timed, frames))
     reset()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    att = 0.0
+    clock = CallClock(L)
+    byt = flo = 0.0
     for t in range(frames):
-        step(t, ev)
-        ev[1].synchronize()
-        att += ev[0].elapsed_time(ev[1]) * 1e-3
-    n = frames * L
+        step(t, clock)
+        byt += B * L * attn_bytes(tok, stream_lk(t), c["heads"])
+        flo += B * L * attn_flops(tok, stream_lk(t), c["heads"])
+    n = clock.calls
     tf = flops / el / 1e12
-    ach = byts / att / 1e9
-    log(f"[bench] stream_batched: {el / frames * 1e3:.2f} ms per frame step, {B * frames / el:.1f} frames/s over "
-        f"{B} streams, {tf:.1f} TFLOP/s; batched calls {att / n * 1e6:.1f} us avg ({ach:.0f} GB/s, "
-        f"{flops / att / 1e12:.1f} TFLOP/s)")
-    return {
-        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / frames * 1e3, "frames_per_s": B * frames / el,
-        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+    ach = byt / clock.kernel_s / 1e9
+    log(f"[bench] stream_batched: {el / timed * 1e3:.2f} ms per frame step, {B * timed / el:.1f} frames/s over "
+        f"{B} streams, {tf:.1f} TFLOP/s; batched kernel {clock.kernel_s / n * 1e6:.1f} us avg ({ach:.0f} GB/s), "
+        f"call {clock.call_s / n * 1e6:.1f} us")
+    res = {
+        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / timed * 1e3, "frames_per_s": B * timed / el,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS, "dtype": "bf16",
         "config": {"workload": f"lingbot_stream_batched: {B} streams x 24 layer caches, 16 heads x 64, bf16, "
-                               f"262 queries/stream/step, {frames} frames, one attention launch per layer and frame",
-                   "streams": B, "layers": L, "frames": frames},
+                               f"262 queries/stream/step, {frames} frames streamed, the last {timed} timed, one "
+                               "attention launch per layer and frame",
+                   "streams": B, "layers": L, "frames": frames, "timed_frames": timed},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                     "traffic": None, "kernel": "batched attention call (attn_bf16_kernel + attn_merge16_kernel)",
-                     "avg_call_us": att / n * 1e6, "calls": n, "attn_tflops": flops / att / 1e12},
+                     "traffic": None, "kernel": "attn_bf16_kernel (batched)", "per_launch_bytes": byt / n,
+                     "avg_kernel_us": clock.kernel_s / n * 1e6, "avg_call_us_with_merge": clock.call_s / n * 1e6,
+                     "calls": n, "kernel_tflops": flo / clock.kernel_s / 1e12},
     }
+    if not args.no_cpu_baseline and args.cpu_sample > 0:
+        sec, fl, nfr = oracle_stream_sample(frames, args.cpu_sample)
+        res["cpu_baseline"] = cpu_baseline(
+            fl / sec / 1e12, "TFLOP/s",
+            f"one stream, 1 of 24 layers, frames {frames - nfr}..{frames - 1} (append + gather + fp64 attention), "
+            f"{sec:.1f} s; the batch's streams are independent, so the rate carries over", sec,
+            {"frames_per_s": 1.0 / (sec / nfr * L)})
+    return res
 
 
 # ----------------------------------------------------------------------------
-# VGGT-style chunked global attention and full global + frame attention
+# Full global attention over 100 frames, then per-frame attention
 # ----------------------------------------------------------------------------
-VGGT_TOKENS = 1374
-CHUNK = dict(layers=24, heads=16, d=64, page=256, frames_per_chunk=8, window_chunks=4)
+def oracle_global_sample(query_rows: int = 256, seed: int = 0):
+    """The oracle on a slice of the global workload: one layer, all 16 heads.
 
-
-def run_chunked(args) -> dict:
-    """Chunks of 8 frames (10,992 tokens, 43 pages) attend to the last 4 chunks (43,968 keys)."""
-    import torch
-    from paged_sliding_window_kv_amd import KvCache, lib
-    c = CHUNK
-    L = c["layers"]
-    tokens = c["frames_per_chunk"] * VGGT_TOKENS
-    W = c["window_chunks"]
-    steps, warm = args.steps, max(args.warmup, W)
-    log(f"[bench] chunked: {L} layers, chunk {tokens} tokens, window {W} chunks, warmup {warm}, timed {steps}")
-    dev = torch.device("cuda:0")
-    lb = lib()
-    caches = [KvCache(num_heads=c["heads"], dtype=args.kv_dtype, patch_tokens=tokens, special_tokens=0,
-                      num_scale_units=0, window_units=W, max_units=warm + steps, device=dev) for _ in range(L)]
-    g = torch.Generator(device=dev)
-    g.manual_seed(1)
-    bank = 2
-    shp = (bank, tokens, c["heads"], c["d"])
-    qs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
-    ks = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
-    vs = [torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
-    out = torch.empty((tokens, c["heads"], c["d"]), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((tokens, c["heads"]), dtype=torch.float32, device=dev)
-    wsb = max(cc.workspace_bytes(tokens) for cc in caches)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    sp = torch.cuda.current_stream(dev).cuda_stream
-
-    kr = args.keep_ratio
-
-    def step(i, events=None):
-        b = i % bank
-        for l in range(L):
-            _ok(lb.kvc_append_frame(caches[l].handle, ks[l][b].data_ptr(), vs[l][b].data_ptr(), sp), "append")
-            if events is not None:
-                events[2 * l].record()
-            if kr < 1.0:
-                # AVGGT-style: each layer its own random page subset (seed = layer)
-                _ok(lb.kvc_attend_subset(caches[l].handle, kr, l, 0, 0, qs[l][b].data_ptr(), tokens, 0.0,
-                                         out.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend_subset")
-            else:
-                _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), tokens, 0.0, out.data_ptr(),
-                                  lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend")
-            if events is not None:
-                events[2 * l + 1].record()
-
-    for i in range(warm):
-        step(i)
-    torch.cuda.synchronize()
-    lk = W * tokens
+    100 frames of 1374 tokens are appended untimed (a bank of 2 distinct frames
+    cycled; values do not change the cost).  Timed: the gather of all 137,400
+    visible keys and the fp64 attention of `query_rows` queries against them,
+    plus one frame's 1374 queries against its own 6 pages.  Returns (seconds,
+    flops of the timed attention).
+    """
+    import synth
+    from oracle import OracleCache, OracleConfig, attention_f64, to_f64
+    H, F = GLOBAL["heads"], GLOBAL["frames"]
+    oc = OracleCache(OracleConfig(num_heads=H, head_dim=64, page_size=256, patch_tokens=VGGT_TOKENS,
+                                  special_tokens=0, num_scale_units=0, window_units=0, max_units=F,
+                                  store_dtype="bf16"))
+    bank = [synth.frame_qkv(seed, 0, i, VGGT_TOKENS, H, 64, "bf16") for i in range(2)]
+    for f in range(F):
+        oc.append(bank[f % 2][1], bank[f % 2][2])
+    q = bank[0][0]
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(warm + i)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    if kr < 1.0:
-        # keys actually attended per layer: the subset keeps the same table positions every steady-state step
-        lks = [int(caches[l].subset_table(kr, l)[1].sum()) for l in range(L)]
-        flops = steps * sum(attn_flops(tokens, x, c["heads"]) for x in lks)
-        lk = sum(lks) / L
-    else:
-        flops = steps * L * attn_flops(tokens, lk, c["heads"])
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
-    att = 0.0
-    for i in range(steps):
-        step(warm + steps + i, ev)
-        ev[-1].synchronize()
-        att += sum(ev[2 * l].elapsed_time(ev[2 * l + 1]) for l in range(L)) * 1e-3
-    n = steps * L
-    ach = flops / att / 1e12
-    tf = flops / el / 1e12
-    log(f"[bench] chunked: {el / steps * 1e3:.2f} ms/step, {tf:.1f} TFLOP/s, attention calls {att / n * 1e6:.1f} us avg, "
-        f"{ach:.1f} TFLOP/s ({ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
-    return {
-        "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3,
-        "frames_per_s": steps * c["frames_per_chunk"] / el,
-        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
-        "config": {"workload": f"vggt_chunked: 24 layer caches, 16 heads x 64, {kv_label(args.kv_dtype)}, "
-                               f"chunks of 8 x 1374 = {tokens} "
-                               f"tokens, window 4 chunks ({W * tokens} visible keys)"
-                               + (f", per-layer page subsets keeping {kr} ({lk:.0f} keys attended)" if kr < 1.0 else "")
-                               + f", {steps} timed chunk steps",
-                   "layers": L, "heads": 16, "head_dim": 64, "chunk_tokens": tokens, "visible_tokens": W * tokens,
-                   "keep_ratio": kr, "attended_tokens": lk, "kv_dtype": args.kv_dtype},
-        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "paged attention call (attn_wide_kernel + attn_merge16_kernel)" if args.kv_dtype == "bf16"
-                               else "paged attention call (attn_bf16_kernel<KV8> + attn_merge16_kernel)",
-                     "avg_call_us": att / n * 1e6, "calls": n,
-                     "bytes_per_call_avg": sum(attn_bytes(tokens, x, c["heads"], kv_elem=kv_elem_bytes(args.kv_dtype))
-                                               for x in ([lk] * L if kr >= 1.0 else lks)) / L},
-    }
+    gk, gv = oc.gather()
+    attention_f64(to_f64(q[:query_rows]), to_f64(gk), to_f64(gv))
+    ids, lens = oc.visible_table()
+    fk, fv = oc.gather(ids[:6], lens[:6])
+    attention_f64(to_f64(q), to_f64(fk), to_f64(fv))
+    sec = time.perf_counter() - t0
+    return sec, attn_flops(query_rows, gk.shape[1], H) + attn_flops(VGGT_TOKENS, fk.shape[1], H)
 
 
 def run_global(args) -> dict:
     """100 frames x 1374 tokens: global attention over all 137,400 tokens, then per-frame attention."""
     import torch
     from paged_sliding_window_kv_amd import KvCache, lib, paged_attention
-    frames, L, H = 100, 24, 16
+    frames, L, H = GLOBAL["frames"], GLOBAL["layers"], GLOBAL["heads"]
     T = frames * VGGT_TOKENS
     steps = max(1, args.steps)
     log(f"[bench] global: {L} layers, {frames} frames x {VGGT_TOKENS} tokens = {T}, timed {steps} pass(es)")
@@ -534,27 +715,38 @@ def run_global(args) -> dict:
     kv = torch.arange(0, frames * upp + 1, upp, dtype=torch.int32, device=dev)
     wsb = max(cc.workspace_bytes(T) for cc in caches)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    # the visible tables of every layer's cache after its 100 appends are the same each pass
+    tabs = []
+    for l in range(L):
+        cc = caches[l]
+        for f in range(frames):
+            cc.append(k[l][f * VGGT_TOKENS:(f + 1) * VGGT_TOKENS], v[l][f * VGGT_TOKENS:(f + 1) * VGGT_TOKENS])
+        ids, lens = cc.visible_table()
+        tabs.append((torch.from_numpy(ids).to(dev), torch.from_numpy(lens).to(dev)))
+    torch.cuda.synchronize()
+    clock_g = CallClock(L)
+    clock_f = CallClock(L)
 
-    def one_pass(events=None):
-        tabs = []
+    def one_pass(timed_calls=False):
         for l in range(L):
             cc = caches[l]
-            cc.reset()
+            _ok(lb.kvc_reset(cc.handle), "reset")
             for f in range(frames):
                 _ok(lb.kvc_append_frame(cc.handle, k[l].data_ptr() + f * fb, v[l].data_ptr() + f * fb, sp), "append")
-            ids, lens = cc.visible_table()
-            tabs.append((torch.from_numpy(ids).to(dev, non_blocking=False), torch.from_numpy(lens).to(dev)))
-            if events is not None:
-                events[4 * l].record()
-            _ok(lb.kvc_attend(cc.handle, q[l].data_ptr(), T, 0.0, out_g.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb,
-                              sp), "attend")
-            if events is not None:
-                events[4 * l + 1].record()
-                events[4 * l + 2].record()
+            if timed_calls:
+                clock_g.before(l)
+            _ok(lb.kvc_attend(cc.handle, q[l].data_ptr(), T, 0.0, out_g.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                              wsb, sp), "attend")
+            if timed_calls:
+                clock_g.after(l)
+                clock_f.before(l)
             paged_attention(q[l], cc.k_pool, cc.v_pool, tabs[l][0], tabs[l][1], qo, kv, VGGT_TOKENS, upp, out=out_f,
-                            lse=None)
-            if events is not None:
-                events[4 * l + 3].record()
+                            lse=None, workspace=ws)
+            if timed_calls:
+                clock_f.after(l)
+        if timed_calls:
+            clock_g.collect(L)
+            clock_f.collect(L)
 
     one_pass()
     torch.cuda.synchronize()
@@ -566,40 +758,49 @@ def run_global(args) -> dict:
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     peak = torch.cuda.max_memory_allocated(dev)
-    # the score matrix one layer's head would need if it were stored (bf16)
-    score_bytes = T * T * 2
+    score_bytes = T * T * 2  # the score matrix one head would need if it were stored (bf16)
     log(f"[bench] global: device memory {base / 2**30:.2f} GiB before the pass, peak {peak / 2**30:.2f} GiB during it "
         f"(one head's {T} x {T} bf16 score matrix alone would be {score_bytes / 2**30:.1f} GiB)")
     fl_g = L * attn_flops(T, T, H)
     fl_f = L * frames * attn_flops(VGGT_TOKENS, VGGT_TOKENS, H)
     tf = steps * (fl_g + fl_f) / el / 1e12
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * L)]
-    one_pass(ev)
-    ev[-1].synchronize()
-    tg = sum(ev[4 * l].elapsed_time(ev[4 * l + 1]) for l in range(L)) * 1e-3
-    tfr = sum(ev[4 * l + 2].elapsed_time(ev[4 * l + 3]) for l in range(L)) * 1e-3
-    ach = fl_g / tg / 1e12
-    log(f"[bench] global: {el / steps:.3f} s/pass, {tf:.1f} TFLOP/s overall; global calls {tg / L * 1e3:.2f} ms avg "
-        f"({ach:.1f} TFLOP/s, {ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak); frame calls {tfr / L * 1e3:.2f} ms avg "
-        f"({fl_f / tfr / 1e12:.1f} TFLOP/s)")
-    return {
+    one_pass(timed_calls=True)
+    kg = clock_g.kernel_s / L
+    ach = fl_g / L / kg / 1e12
+    tfr = clock_f.call_s / L
+    log(f"[bench] global: {el / steps:.3f} s/pass, {tf:.1f} TFLOP/s overall; global kernel {kg * 1e3:.2f} ms avg "
+        f"({ach:.1f} TFLOP/s, {ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak); frame calls {tfr * 1e3:.2f} ms avg "
+        f"({fl_f / L / tfr / 1e12:.1f} TFLOP/s)")
+    res = {
         "value": tf, "unit": "TFLOP/s", "ms_per_step": el / steps * 1e3, "frames_per_s": steps * frames / el,
-        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+        "pct_bf16_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS, "dtype": "bf16",
         "config": {"workload": f"vggt_global: 24 layers, 100 frames x 1374 tokens = {T}, 16 heads x 64, bf16, "
-                               "global attention (no mask) + per-frame attention per layer, appends included",
-                   "layers": L, "heads": H, "head_dim": 64, "tokens": T,
+                               "global attention (no mask) + per-frame attention per layer, appends included; "
+                               "step = one pass over 24 layers",
+                   "layers": L, "heads": H, "head_dim": 64, "tokens": T, "global_table_pages": len(tabs[0][0]),
                    "device_memory_gib": base / 2**30, "peak_device_memory_gib": peak / 2**30,
                    "score_matrix_one_head_gib": score_bytes / 2**30},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "global attention call (attn_wide_kernel)", "avg_call_us": tg / L * 1e6, "calls": L,
-                     "frame_attn_tflops": fl_f / tfr / 1e12},
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "attn_wide_kernel (global)",
+                     "per_launch_flops": fl_g / L, "avg_kernel_us": kg * 1e6,
+                     "avg_call_us_with_merge": clock_g.call_s / L * 1e6, "calls": L,
+                     "frame_attn_tflops": fl_f / L / tfr / 1e12},
     }
+    if not args.no_cpu_baseline:
+        rows = max(1, args.cpu_rows // 4)
+        sec, fl = oracle_global_sample(rows)
+        rate = fl / sec / 1e12
+        res["cpu_baseline"] = cpu_baseline(
+            rate, "TFLOP/s",
+            f"1 of 24 layers, all 16 heads: {rows} queries against all {T} keys plus one frame's 1374 queries "
+            f"against its own pages (gather + fp64 attention), {sec:.1f} s; extrapolated to a pass by the FLOP ratio",
+            sec, {"extrapolated": True, "frames_per_s": frames / ((fl_g + fl_f) / (rate * 1e12))})
+    return res
 
 
-KEYFRAME = dict(heads=4, d=64, page=256, patch=256, special=6, scale=2, window=4, interval=4, frames=10000)
-
-
+# ----------------------------------------------------------------------------
+# Keyframe stream (fp32)
+# ----------------------------------------------------------------------------
 def keyframe_kept(t: int, c=KEYFRAME) -> bool:
     """Frame t's unit stays in the cache: the scale frames, then every interval-th frame."""
     return t < c["scale"] or (t - c["scale"]) % c["interval"] == 0
@@ -609,6 +810,29 @@ def keyframe_lk(units: int, c=KEYFRAME) -> int:
     """Visible tokens with `units` units in the cache: scale + window patches, and the
     special tokens of every unit (special pages are never evicted)."""
     return (min(units, c["scale"]) + min(max(units - c["scale"], 0), c["window"])) * c["patch"] + units * c["special"]
+
+
+def oracle_keyframe_sample(frames: int, seed: int = 0):
+    """The oracle on the first `frames` frames of the keyframe stream (append, fp64 attention, rollback)."""
+    import synth
+    from oracle import OracleCache, OracleConfig, attention_f64, to_f64
+    c = KEYFRAME
+    tok = c["patch"] + c["special"]
+    oc = OracleCache(OracleConfig(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"],
+                                  patch_tokens=c["patch"], special_tokens=c["special"], num_scale_units=c["scale"],
+                                  window_units=c["window"], max_units=frames, store_dtype="f32"))
+    bank = [synth.frame_qkv(seed, 0, i, tok, c["heads"], c["d"], "f32") for i in range(4)]
+    fl = 0.0
+    t0 = time.perf_counter()
+    for t in range(frames):
+        q, k, v = bank[t % 4]
+        oc.append(k, v)
+        gk, gv = oc.gather()
+        attention_f64(to_f64(q), to_f64(gk), to_f64(gv))
+        fl += attn_flops(tok, gk.shape[1], c["heads"], c["d"])
+        if not keyframe_kept(t):
+            oc.rollback()
+    return time.perf_counter() - t0, fl
 
 
 def run_keyframe(args) -> dict:
@@ -627,7 +851,7 @@ def run_keyframe(args) -> dict:
     dev = torch.device("cuda:0")
     cache = KvCache(num_heads=H, head_dim=d, page_size=c["page"], dtype="f32", patch_tokens=c["patch"],
                     special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
-                    max_units=frames, device=dev)
+                    max_units=max(frames, args.warmup, 1), device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     bank = 4
@@ -644,18 +868,18 @@ def run_keyframe(args) -> dict:
     vp = [v.data_ptr() + i * fb for i in range(bank)]
     op, lp, wsp = o.data_ptr(), lse.data_ptr(), ws.data_ptr()
 
-    def frame(t, ev=None):
+    def frame(t, clock=None, slot=0):
         b = t % bank
         _ok(L.kvc_append_frame(h, kp[b], vp[b], sp), "kvc_append_frame")
-        if ev is not None:
-            ev[0].record()
+        if clock is not None:
+            clock.before(slot)
         _ok(L.kvc_attend(h, qp[b], tok, 0.0, op, lp, wsp, wsb, sp), "kvc_attend")
-        if ev is not None:
-            ev[1].record()
+        if clock is not None:
+            clock.after(slot)
         if not keyframe_kept(t):
             _ok(L.kvc_rollback_last_frame(h), "kvc_rollback_last_frame")
 
-    for t in range(min(args.warmup, frames)):
+    for t in range(args.warmup):
         frame(t)
     torch.cuda.synchronize()
     cache.reset()
@@ -676,41 +900,52 @@ def run_keyframe(args) -> dict:
         total_flops += attn_flops(tok, lk, H, d)
         kept += keyframe_kept(t)
     assert st["num_units"] == kept, (st["num_units"], kept)
-    assert len(st["scale_pages"]) + len(st["window_pages"]) == c["scale"] + c["window"]
+    assert len(st["scale_pages"]) + len(st["window_pages"]) == min(kept, c["scale"] + c["window"])
     assert mem1 == mem0, (mem0, mem1)
     fps = frames / elapsed
     log(f"[bench] keyframe: {frames} frames in {elapsed:.3f} s, {fps:.0f} frames/s, "
         f"{total_flops / elapsed / 1e12:.2f} TFLOP/s; {kept} units kept, device memory unchanged")
     # attention calls alone, replayed with events around each call
     cache.reset()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
-    att = 0.0
-    for t0_ in range(0, frames, len(evs)):
-        n = min(len(evs), frames - t0_)
+    chunk = 64
+    clock = CallClock(chunk)
+    for t0_ in range(0, frames, chunk):
+        n = min(chunk, frames - t0_)
         for i in range(n):
-            frame(t0_ + i, evs[i])
-        torch.cuda.synchronize()
-        att += sum(evs[i][0].elapsed_time(evs[i][1]) for i in range(n)) * 1e-3
-    ach = total_flops / att / 1e12
-    log(f"[bench] keyframe attention calls: {att / frames * 1e6:.2f} us avg, {ach:.2f} TFLOP/s (fp32 MFMA)")
-    peak_f32 = 157.3  # MI355X dense fp32 MFMA
-    return {
+            frame(t0_ + i, clock, i)
+        clock.collect(n)
+    ach = total_flops / clock.kernel_s / 1e12
+    log(f"[bench] keyframe attention: kernel {clock.kernel_s / frames * 1e6:.2f} us avg, {ach:.2f} TFLOP/s "
+        f"(fp32 matrix cores)")
+    res = {
         "value": fps, "unit": "frames/s", "ms_per_step": elapsed / frames * 1e3, "frames_per_s": fps,
         "dtype": "f32",
         "pct_bf16_mfma_peak": None,
         "config": {"workload": f"keyframe_stream: 1 layer cache, {H} heads x {d}, fp32, 256 patch + 6 special "
                                f"tokens/frame, {c['scale']} scale frames, {c['window']}-frame window, keyframe "
-                               f"every {c['interval']} frames (others rolled back), 262 queries/step, {frames} frames",
+                               f"every {c['interval']} frames (others rolled back), 262 queries/step, {frames} "
+                               "frames; step = one frame (append, attention, rollback)",
                    "layers": 1, "heads": H, "head_dim": d, "page_size": c["page"], "frames": frames,
                    "units_kept": kept, "rollbacks": frames - kept, "max_visible_tokens": max(lks),
                    "tflops_whole_step": total_flops / elapsed / 1e12,
                    "device_memory_growth_bytes": mem1 - mem0},
-        "roofline": {"bound": "mfma", "achieved": ach, "peak": peak_f32, "unit": "TFLOP/s", "frac": ach / peak_f32,
-                     "traffic": None, "kernel": "attn_f32_kernel (+ attn_merge_kernel when split)",
-                     "avg_call_us": att / frames * 1e6, "calls": frames},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_F32_TFLOPS, "traffic": None, "kernel": "attn_f32_kernel",
+                     "avg_kernel_us": clock.kernel_s / frames * 1e6,
+                     "avg_call_us_with_merge": clock.call_s / frames * 1e6, "calls": frames},
     }
+    if not args.no_cpu_baseline:
+        n = min(frames, 2000)
+        sec, fl = oracle_keyframe_sample(n)
+        res["cpu_baseline"] = cpu_baseline(n / sec, "frames/s",
+                                           f"frames 0..{n - 1} of the keyframe stream (append, fp64 attention, "
+                                           f"rollback), {sec:.1f} s", sec, {"tflops": fl / sec / 1e12})
+    return res
 
 
+# ----------------------------------------------------------------------------
+# counter calibration and profile bookkeeping
+# ----------------------------------------------------------------------------
 def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
     """A plain device-to-device copy of known size (reference for the FETCH_SIZE/WRITE_SIZE counters)."""
     import torch
@@ -727,14 +962,14 @@ def attn_source_hash() -> str:
     """Hash of the attention kernels' source and of the build script (whose flags shape the generated code)."""
     import hashlib
     h = hashlib.sha256()
-    for rel in (("csrc", "attn_bf16.hip"), ("build.py",)):
+    for rel in (("csrc", "attn_bf16.hip"), ("csrc", "kernels.hpp"), ("build.py",)):
         with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", *rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic_ratio(name: str):
-    """HBM bytes over algorithmic bytes per call, from a committed counter summary.
+    """HBM bytes over algorithmic bytes per launch, from a committed counter summary.
 
     The summary holds lines `kernel_source_sha256_16: <hash>` and
     `traffic_ratio: <ratio>`.  None if the kernel source changed since the
@@ -755,15 +990,29 @@ def measured_traffic_ratio(name: str):
         return None
 
 
-def main():
+def add_traffic(res: dict, summary: str) -> None:
+    ratio = measured_traffic_ratio(summary)
+    rf = res["roofline"]
+    if ratio is not None and "per_launch_bytes" in rf:
+        rf["traffic"] = ratio * rf["per_launch_bytes"]
+        rf["traffic_ratio"] = ratio
+        rf["traffic_source"] = f"profiles/{summary}"
+
+
+DEFAULT_STEPS = {"chunked": 20, "stream": STREAM["frames"], "global": 1, "stream_batched": STREAM["frames"],
+                 "keyframe": KEYFRAME["frames"]}
+
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps: frames (stream, default 1000), chunk steps (chunked, default 8) or "
-                         "passes (global, default 1)")
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="stream",
-                    choices=["stream", "chunked", "global", "stream_batched", "keyframe"])
+                    help="timed steps: chunk steps at the full window (chunked, default 20), the last K frames of "
+                         "the 1,000-frame stream (stream, stream_batched), passes (global, default 1), frames "
+                         "(keyframe, default 10,000)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps before timing (chunked: at least 4)")
+    ap.add_argument("--workload", default="chunked",
+                    choices=["chunked", "stream", "global", "stream_batched", "keyframe"])
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
@@ -771,10 +1020,24 @@ def main():
                          "RFC section 3.4)")
     ap.add_argument("--keep-ratio", type=float, default=1.0,
                     help="chunked: attend to a per-layer random page subset keeping this fraction (AVGGT-style)")
+    ap.add_argument("--no-extras", action="store_true", help="chunked: skip the LingBot stream and the probes")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=40, help="frames of one layer the oracle times")
-    args = ap.parse_args()
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="chunked/global oracle slice: query rows of one layer (all heads)")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="stream oracle sample: last frames of one layer")
+    args = ap.parse_args(argv)
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS[args.workload]
+    if args.steps < 1:
+        ap.error("--steps must be at least 1")
+    if args.warmup < 0:
+        ap.error("--warmup must be non-negative")
+    return args
+
+
+def main(argv=None):
+    args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
               "mode: the cache and kernels run on one device)", file=sys.stderr)
@@ -786,28 +1049,38 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    if args.steps is None:
-        args.steps = {"stream": 1000, "chunked": 8, "global": 1, "stream_batched": 1000,
-                      "keyframe": KEYFRAME["frames"]}[args.workload]
-    if args.workload == "stream":
-        res = run_stream(args)
-        ratio = measured_traffic_ratio("attn_bf16_lingbot_stream_traffic.md") if args.kv_dtype == "bf16" else None
-        if ratio is not None:
-            res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
-            res["roofline"]["traffic_ratio"] = ratio
-    elif args.workload == "chunked":
+    extras = {}
+    if args.workload == "chunked":
         res = run_chunked(args)
-        ratio = (measured_traffic_ratio("attn_wide_vggt_chunked.md")
-                 if args.keep_ratio >= 1.0 and args.kv_dtype == "bf16" else None)
-        if ratio is not None:
-            res["roofline"]["traffic"] = ratio * res["roofline"]["bytes_per_call_avg"]
-            res["roofline"]["traffic_ratio"] = ratio
+        if args.keep_ratio >= 1.0 and args.kv_dtype == "bf16":
+            add_traffic(res, "attn_wide_vggt_chunked.md")
+        if not args.no_extras:
+            st = run_stream(args, cpu_sample=args.cpu_sample)
+            if args.kv_dtype == "bf16":
+                add_traffic(st, "attn_bf16_lingbot_stream_traffic.md")
+            extras["lingbot_stream"] = {k: st[k] for k in ("value", "unit", "ms_per_step", "frames_per_s",
+                                                           "pct_bf16_mfma_peak", "config", "roofline")}
+            if "cpu_baseline" in st:
+                extras["lingbot_stream"]["cpu_baseline"] = st["cpu_baseline"]
+    elif args.workload == "stream":
+        res = run_stream(args, timed=args.steps)
+        if args.kv_dtype == "bf16":
+            add_traffic(res, "attn_bf16_lingbot_stream_traffic.md")
     elif args.workload == "stream_batched":
         res = run_stream_batched(args)
     elif args.workload == "keyframe":
         res = run_keyframe(args)
     else:
         res = run_global(args)
+    probes = None
+    if not args.no_extras:
+        probes = run_probes()
+        rf = res["roofline"]
+        meas = probes["mfma_bf16_tflops"] if rf["unit"] == "TFLOP/s" and rf["peak"] == PEAK_BF16_TFLOPS else (
+            probes["hbm_read_gbs"] if rf["unit"] == "GB/s" else None)
+        if meas:
+            rf["peak_measured"] = meas
+            rf["frac_of_measured"] = rf["achieved"] / meas
     out = {
         "metric": METRIC,
         "value": res["value"],
@@ -828,6 +1101,10 @@ def main():
     }
     if "cpu_baseline" in res:
         out["cpu_baseline"] = res["cpu_baseline"]
+    if extras:
+        out["extras"] = extras
+    if probes:
+        out["probes"] = probes
     out["kernel_source_sha256_16"] = attn_source_hash()
     print(json.dumps(out), flush=True)
 

@@ -62,8 +62,16 @@
  *
  * Errors
  *   Every call returns KVC_OK (0) or a negative kvc_status.  On error the
- *   handle's state is unchanged.  kvc_last_error() gives a thread-local
- *   message for the last failing call on the calling thread.
+ *   handle's state is unchanged (the one exception, a windowed restart that
+ *   fails on the device, is stated at kvc_windowed_append).  No C++ exception
+ *   leaves the library: host allocation failures give KVC_ERR_HOST_MEMORY.
+ *   kvc_last_error() gives a thread-local message for the last failing call
+ *   on the calling thread.
+ *
+ * Passages cited below
+ *   "LingBot-Map Paged KV Cache" (a Chinese-language article; section n is
+ *   its n-th numbered section, section 0 its lead paragraph) and "vLLM-Omni
+ *   RFC #2727: Reconstruction Engine" (RFC #2727, sections 1-3).
  */
 #ifndef KVC_H_
 #define KVC_H_
@@ -85,6 +93,8 @@ typedef enum kvc_status {
   KVC_ERR_BUFFER_TOO_SMALL = -4,
   KVC_ERR_UNSUPPORTED = -5,
   KVC_ERR_DEVICE = -6,
+  KVC_ERR_HOST_MEMORY = -7, /* a host allocation failed */
+  KVC_ERR_INTERNAL = -8,    /* an unexpected internal error (a bug) */
 } kvc_status;
 
 typedef enum kvc_dtype { KVC_DTYPE_BF16 = 0, KVC_DTYPE_F32 = 1, KVC_DTYPE_FP8_E4M3 = 2 } kvc_dtype;
@@ -134,21 +144,39 @@ typedef struct kvc_state {
 
 typedef struct kvc_cache kvc_t;
 
-/* Pages a cache with this config needs: with a bounded window,
- * min(max_units, S + W + 1) units of ceil(patch_tokens / P) pages (one unit
- * more than the window holds, since an append pops before it evicts), plus the
- * special pages of max_units units; with an unbounded window, max_units units. */
+/* Pages a cache with this config needs ("LingBot-Map Paged KV Cache",
+ * section 0: cache memory stays constant over 10,000+ frames; section 2: the
+ * patch cache holds the scale and window frames' pages, each frame's 256
+ * patch tokens fill one page, and special pages pack 42 frames each): with a
+ * bounded window, min(max_units, S + W + 1) units of ceil(patch_tokens / P)
+ * pages (one unit more than the window holds, since an append pops before it
+ * evicts), plus the special pages of max_units units; with an unbounded
+ * window (RFC #2727, section 2.3: an infinite window is full global
+ * attention), max_units units.  *num_pages receives the count.
+ * KVC_ERR_INVALID_ARGUMENT for an invalid config or a count past int32. */
 int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages);
 
-/* Bytes of one pool (K or V): num_pages * H * P * d * sizeof(element); for
- * FP8 caches num_pages * H * P * (d + 1) (codes and row exponents). */
+/* Bytes of one pool (K or V) for cfg (num_pages, or kvc_required_pages when
+ * 0): num_pages * H * P * d * sizeof(element); for FP8 caches
+ * num_pages * H * P * (d + 1) (codes and row exponents).  The caller
+ * allocates the pools once at this size; nothing grows afterwards
+ * ("LingBot-Map Paged KV Cache", section 0: constant cache memory). */
 int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes);
 
-/* Create a cache.  k_pool / v_pool: caller-owned device buffers of
- * kvc_pool_bytes each (layouts above), or both NULL for a host-only handle
- * that tracks metadata without device work (appends then take NULL K/V).
- * The pools are not cleared.  *out receives the handle. */
+/* Create a cache: one layer's page pool, free list and three page streams
+ * ("LingBot-Map Paged KV Cache", section 2: each layer's KV is cut into
+ * fixed-size pages; a fresh free list pops pages 0, 1, 2, ...).  k_pool /
+ * v_pool: caller-owned device buffers of kvc_pool_bytes each (layouts above),
+ * or both NULL for a host-only handle that tracks metadata without device
+ * work (appends then take NULL K/V).  The pools are not cleared.  All host
+ * metadata is sized here: later calls on the handle allocate nothing except
+ * the pinned staging of tables longer than 640 entries (see kvc_attend).
+ * *out receives the handle.  KVC_ERR_UNSUPPORTED for device pools with
+ * head_dim != 64, page_size not a multiple of 64 or units of more than 256
+ * pages. */
 int kvc_create(const kvc_config* cfg, void* k_pool, void* v_pool, kvc_t** out);
+/* Release the handle's host metadata (the pools stay the caller's).  Waits
+ * for table uploads still in flight.  NULL is accepted. */
 int kvc_destroy(kvc_t* cache);
 
 /* Append one unit ("LingBot-Map Paged KV Cache", section 2; RFC #2727,
@@ -157,8 +185,10 @@ int kvc_destroy(kvc_t* cache);
  * patch tokens first, in the cache dtype (bf16 for FP8 caches, quantised by
  * the append); both NULL on a host-only handle.  Both 16-byte aligned
  * (KVC_ERR_INVALID_ARGUMENT otherwise).
- * Plans on the host and enqueues one scatter kernel on `stream`.
- * KVC_ERR_OUT_OF_PAGES when the free list cannot supply the unit. */
+ * Plans on the host, enqueues one scatter kernel on `stream`, and only
+ * then commits the plan: KVC_ERR_OUT_OF_PAGES when the free list cannot
+ * supply the unit, KVC_ERR_DEVICE when the launch fails, the cache unchanged
+ * in both cases. */
 int kvc_append_frame(kvc_t* cache, const void* k_unit, const void* v_unit, kvc_stream_t stream);
 
 /* Undo the last append exactly ("LingBot-Map Paged KV Cache", section 3: a
@@ -167,7 +197,9 @@ int kvc_append_frame(kvc_t* cache, const void* k_unit, const void* v_unit, kvc_s
  * KVC_ERR_NO_UNDO if there is nothing to undo. */
 int kvc_rollback_last_frame(kvc_t* cache);
 
-/* Drop every unit and restore the fresh free-list order. */
+/* Drop every unit and restore the fresh free-list order: the once-per-window
+ * reset of windowed inference ("LingBot-Map Paged KV Cache", section 4;
+ * kvc_windowed_append calls it).  Host-only; device pages keep their bytes. */
 int kvc_reset(kvc_t* cache);
 
 /* Visible page table ("LingBot-Map Paged KV Cache", section 2): scale pages
@@ -181,7 +213,12 @@ int kvc_reset(kvc_t* cache);
 int kvc_build_visible_table(const kvc_t* cache, int32_t* page_ids, int32_t* page_lens,
                             int32_t capacity, int32_t* num_pages, int32_t* last_page_len);
 
-/* Copy of the metadata; see kvc_state. */
+/* Copy of the metadata; see kvc_state.  It exposes what the pages' invariants
+ * are stated on ("LingBot-Map Paged KV Cache", section 2: patch pages constant
+ * after warm-up, out-of-window pages back on the free list, special pages
+ * growing one per 42 frames; section 3: a rollback restores the state).
+ * KVC_ERR_BUFFER_TOO_SMALL when out->capacity < the pool's page count and any
+ * array pointer is set. */
 int kvc_get_state(const kvc_t* cache, kvc_state* out);
 
 /* ------------------------------------------------------------------------ */
@@ -215,11 +252,17 @@ typedef struct paged_attn_args {
   size_t workspace_bytes;
 } paged_attn_args;
 
-/* Workspace bytes paged_attn_fwd needs for these arguments (split-key
- * partial outputs and log-sum-exps).  Reads only host fields of args. */
+/* Workspace bytes paged_attn_fwd needs for these arguments: split-key partial
+ * outputs and log-sum-exps.  A sequence's key range may be cut into splits
+ * that run on separate workgroups and are merged by log-sum-exp weights, the
+ * same merge ring attention uses across devices (RFC #2727, section 3.4:
+ * ring attention over the in-window KV); the split count is chosen by a
+ * model of workgroup rounds.  Enough for every table of up to max_kv_pages
+ * entries per sequence.  Reads only host fields of args. */
 int paged_attn_workspace_size(const paged_attn_args* args, size_t* bytes);
 
-/* Split count paged_attn_fwd will use for these arguments. */
+/* Split count paged_attn_fwd will use for these arguments (num_splits, when
+ * set, clamped to [1, max_kv_pages]; else the library's choice). */
 int paged_attn_num_splits(const paged_attn_args* args, int32_t* num_splits);
 
 /* O = softmax(sm_scale * Q K^T) V per sequence and head over the tokens of
@@ -233,8 +276,9 @@ int paged_attn_fwd(const paged_attn_args* args, kvc_stream_t stream);
  * O_i and its log-sum-exp lse_i; writes O = sum_i exp(lse_i - lse) O_i with
  * lse = log sum_i exp(lse_i).  partial_o: device fp32 [num_parts][rows][H][d],
  * partial_lse: device fp32 [num_parts][rows][H]; o in `dtype`, lse nullable.
- * Exposed for testing the merge on its own; paged_attn_fwd calls it when it
- * splits.  partial_o and o must be 16-byte aligned (KVC_ERR_INVALID_ARGUMENT
+ * This is the combine step of attention computed over disjoint key subsets
+ * (RFC #2727, section 3.4: ring attention shards the in-window KV).  Exposed
+ * for testing the merge on its own; paged_attn_fwd calls it when it splits.  partial_o and o must be 16-byte aligned (KVC_ERR_INVALID_ARGUMENT
  * otherwise). */
 int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
                      const float* partial_o, const float* partial_lse, void* o, float* lse,
@@ -248,10 +292,18 @@ int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num
  * [num_q][H][d] in the cache dtype; lse: device [num_q][H] fp32 or NULL;
  * sm_scale <= 0 means 1/sqrt(d).  workspace: device scratch of
  * kvc_attend_workspace_size bytes (enough for any state of this cache).
- * KVC_ERR_UNSUPPORTED when the table has more than 640 entries: build it
- * with kvc_build_visible_table and call paged_attn_fwd instead. */
+ * Tables of up to 640 entries travel in the launch arguments.  Longer ones
+ * (a LingBot stream past about 23,900 frames, whose special pages keep
+ * growing, "LingBot-Map Paged KV Cache", section 2) are written to pinned
+ * host memory the handle owns (a ring of 16 slots, allocated on the first
+ * such call) and copied asynchronously to the start of the workspace on
+ * `stream`; the host waits only when a slot's copy from 16 calls earlier has
+ * not yet completed. */
 int kvc_attend(const kvc_t* cache, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
                void* workspace, size_t workspace_bytes, kvc_stream_t stream);
+/* Workspace bytes kvc_attend and kvc_attend_subset need for num_q queries on
+ * this cache, for any table it can hold (the split partials of the largest
+ * split count, plus the table region when tables can exceed 640 entries). */
 int kvc_attend_workspace_size(const kvc_t* cache, int32_t num_q, size_t* bytes);
 
 /* Page-subset table ("vLLM-Omni RFC #2727: Reconstruction Engine", section
@@ -271,7 +323,8 @@ int kvc_build_subset_table(const kvc_t* cache, float keep_ratio, uint64_t seed, 
                            int32_t keep_last, int32_t* page_ids, int32_t* page_lens, int32_t capacity,
                            int32_t* num_pages);
 /* kvc_attend over that subset table instead of the full visible table (same
- * arguments, workspace of kvc_attend_workspace_size bytes). */
+ * arguments, workspace of kvc_attend_workspace_size bytes; RFC #2727, section
+ * 3.4: attention over a per-layer random KV subset). */
 int kvc_attend_subset(const kvc_t* cache, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
                       const void* q, int32_t num_q, float sm_scale, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, kvc_stream_t stream);
@@ -301,13 +354,85 @@ int kvc_attend_subset(const kvc_t* cache, float keep_ratio, uint64_t seed, int32
 int kvc_attend_batch(const kvc_t* const* caches, int32_t num_caches, const void* q, const int32_t* qo_indptr,
                      float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
                      kvc_stream_t stream);
+/* Workspace bytes kvc_attend_batch needs for these caches in their current
+ * state and these query offsets (RFC #2727, sections 3.2-3.3). */
 int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_caches, const int32_t* qo_indptr,
                                     size_t* bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Windowed inference ("LingBot-Map Paged KV Cache", section 4)              */
+/* ------------------------------------------------------------------------ */
+
+/* The page restarts the KV cache once per window of window_size KV slots
+ * (stored units, not raw frames; 128 in its long run) and lets adjacent
+ * windows share overlap_keyframes units.  Reading used: a slot is a kept
+ * unit.  When a window holds window_slots kept units, the next append first
+ * resets the cache and re-appends the last `overlap` kept units of the
+ * finished window, oldest first, with the K/V they were appended with; a
+ * dropped unit (keyframe skip, section 3) takes no slot.  The K/V of the last
+ * `overlap` kept units wait in two caller-owned device rings, so device
+ * memory stays fixed however long the stream runs.
+ *
+ * A windowed handle drives one cache; while it exists, append, roll back and
+ * reset that cache only through it (attention calls on the cache are fine).
+ * The cache must outlive the windowed handle. */
+typedef struct kvc_windowed kvc_windowed_t;
+
+typedef struct kvc_windowed_state {
+  int32_t slots;       /* kept units in the current window */
+  int32_t windows;     /* restarts so far */
+  int32_t ring_units;  /* kept units waiting in the ring (at most overlap) */
+  int32_t pending;     /* 1 if an appended unit waits for keep or drop */
+} kvc_windowed_state;
+
+/* Bytes of each ring (K and V) for `overlap` units of this cache:
+ * overlap * (patch_tokens + special_tokens) * H * d * activation element
+ * size (bf16 for bf16 and FP8 caches, fp32 for fp32 caches); 0 for a
+ * host-only cache. */
+int kvc_windowed_ring_bytes(const kvc_t* cache, int32_t overlap, size_t* bytes);
+
+/* Windowed driver over `cache`.  1 <= window_slots, 0 <= overlap <
+ * window_slots.  k_ring / v_ring: device buffers of kvc_windowed_ring_bytes
+ * each, 16-byte aligned (NULL when overlap is 0 or the cache is host-only).
+ * KVC_ERR_INVALID_ARGUMENT if the pool cannot hold window_slots + 1 units
+ * (the kept units plus the one waiting for keep or drop). */
+int kvc_windowed_create(kvc_t* cache, int32_t window_slots, int32_t overlap, void* k_ring, void* v_ring,
+                        kvc_windowed_t** out);
+int kvc_windowed_destroy(kvc_windowed_t* w);
+
+/* Append one unit (K/V as kvc_append_frame takes them).  When the window is
+ * full, first restarts it as described above; *restarted (nullable) is set to
+ * 1 then, else 0.  The unit then waits for kvc_windowed_keep or
+ * kvc_windowed_drop, and k_unit / v_unit must hold their data until that call
+ * is enqueued on the stream (keep copies them into the ring).  Errors:
+ * KVC_ERR_INVALID_ARGUMENT while a unit is waiting; if a restart fails on
+ * the device, KVC_ERR_DEVICE and the windowed handle refuses every later
+ * append (the cache is then part-way through a restart). */
+int kvc_windowed_append(kvc_windowed_t* w, const void* k_unit, const void* v_unit, kvc_stream_t stream,
+                        int32_t* restarted);
+/* The waiting unit is a keyframe: it stays, takes one slot, and its K/V are
+ * copied into the ring on `stream` (when overlap > 0). */
+int kvc_windowed_keep(kvc_windowed_t* w, kvc_stream_t stream);
+/* The waiting unit is not kept ("LingBot-Map Paged KV Cache", section 3):
+ * it is rolled back and takes no slot. */
+int kvc_windowed_drop(kvc_windowed_t* w);
+int kvc_windowed_get_state(const kvc_windowed_t* w, kvc_windowed_state* out);
+
+/* ------------------------------------------------------------------------ */
+/* Errors, version, measurement                                              */
+/* ------------------------------------------------------------------------ */
 
 const char* kvc_strerror(int status);
 const char* kvc_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */
 int kvc_version(void);
+
+/* Measurement hook for timing the attention kernel apart from the merge of
+ * split partials: while `event` (a hipEvent_t) is not NULL, every attention
+ * call made on the calling thread records it on its launch stream right after
+ * the attention kernel and before the merge.  An event recorded before the
+ * call and this one then bracket the kernel alone.  NULL turns it off. */
+int kvc_set_kernel_done_event(void* event);
 
 #ifdef __cplusplus
 }

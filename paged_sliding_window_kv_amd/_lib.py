@@ -19,6 +19,8 @@ KVC_ERR_NO_UNDO = -3
 KVC_ERR_BUFFER_TOO_SMALL = -4
 KVC_ERR_UNSUPPORTED = -5
 KVC_ERR_DEVICE = -6
+KVC_ERR_HOST_MEMORY = -7
+KVC_ERR_INTERNAL = -8
 
 KVC_DTYPE_BF16 = 0
 KVC_DTYPE_F32 = 1
@@ -32,7 +34,11 @@ EXPORTED = (
     "paged_attn_workspace_size", "paged_attn_num_splits", "paged_attn_fwd", "paged_attn_merge",
     "kvc_attend", "kvc_attend_workspace_size", "kvc_attend_batch", "kvc_attend_batch_workspace_size",
     "kvc_build_subset_table", "kvc_attend_subset",
-    "kvc_strerror", "kvc_last_error", "kvc_version",
+    "kvc_windowed_ring_bytes", "kvc_windowed_create", "kvc_windowed_destroy", "kvc_windowed_append",
+    "kvc_windowed_keep", "kvc_windowed_drop", "kvc_windowed_get_state",
+    "kvc_strerror", "kvc_last_error", "kvc_version", "kvc_set_kernel_done_event",
+    # include/kvc_probe.h
+    "kvc_probe_scratch_bytes", "kvc_probe_mfma_bf16", "kvc_probe_hbm",
 )
 MAX_INLINE_PAGES = 640
 MAX_BATCH_CACHES = 16
@@ -61,6 +67,10 @@ class KvcState(C.Structure):
         ("has_undo", C.c_int32),
         ("num_pages", C.c_int32),
     ]
+
+
+class KvcWindowedState(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("slots", "windows", "ring_units", "pending")]
 
 
 class PagedAttnArgs(C.Structure):
@@ -131,6 +141,18 @@ def _declare(lib):
                                         C.c_size_t, vp]),
         "kvc_attend_batch": (C.c_int, [C.POINTER(vp), i32, vp, i32p, C.c_float, vp, vp, vp, C.c_size_t, vp]),
         "kvc_attend_batch_workspace_size": (C.c_int, [C.POINTER(vp), i32, i32p, C.POINTER(C.c_size_t)]),
+        "kvc_windowed_ring_bytes": (C.c_int, [vp, i32, C.POINTER(C.c_size_t)]),
+        "kvc_windowed_create": (C.c_int, [vp, i32, i32, vp, vp, C.POINTER(vp)]),
+        "kvc_windowed_destroy": (C.c_int, [vp]),
+        "kvc_windowed_append": (C.c_int, [vp, vp, vp, vp, i32p]),
+        "kvc_windowed_keep": (C.c_int, [vp, vp]),
+        "kvc_windowed_drop": (C.c_int, [vp]),
+        "kvc_windowed_get_state": (C.c_int, [vp, C.POINTER(KvcWindowedState)]),
+        "kvc_set_kernel_done_event": (C.c_int, [vp]),
+        "kvc_probe_scratch_bytes": (C.c_size_t, []),
+        "kvc_probe_mfma_bf16": (C.c_int, [vp, C.c_size_t, vp, C.POINTER(C.c_double)]),
+        "kvc_probe_hbm": (C.c_int, [vp, vp, C.c_size_t, vp, C.c_size_t, vp, C.POINTER(C.c_double),
+                                    C.POINTER(C.c_double)]),
         "kvc_strerror": (C.c_char_p, [C.c_int]),
         "kvc_last_error": (C.c_char_p, []),
         "kvc_version": (C.c_int, []),

@@ -86,20 +86,22 @@ def paged_attention(q, k_pool, v_pool, page_ids, page_lens, qo_indptr, kv_indptr
             raise ValueError("FP8 pools are uint8 buffers and take bf16 q")
     elif k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
         raise ValueError("q and pools must share a dtype")
-    if out is None:
-        out = t.empty_like(q)
-    if lse is None:
-        lse = t.empty(q.shape[:2], dtype=t.float32, device=q.device)
-    a = make_args(q, k_pool, v_pool, page_ids, page_lens, qo_indptr, kv_indptr, out, lse, max_qo_len,
-                  max_kv_pages, sm_scale, num_splits, fp8_pages)
-    need = workspace_bytes(a)
-    if need:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = t.empty(need, dtype=t.uint8, device=q.device)
-        a.workspace = workspace.data_ptr()
-        a.workspace_bytes = workspace.numel() * workspace.element_size()
-    s = t.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    L.check(L.lib().paged_attn_fwd(C.byref(a), s), "paged_attn_fwd")
+    from .cache import on_stream
+    with on_stream(stream, q.device):
+        # outputs and workspace are allocated on the launch stream
+        if out is None:
+            out = t.empty_like(q)
+        if lse is None:
+            lse = t.empty(q.shape[:2], dtype=t.float32, device=q.device)
+        a = make_args(q, k_pool, v_pool, page_ids, page_lens, qo_indptr, kv_indptr, out, lse, max_qo_len,
+                      max_kv_pages, sm_scale, num_splits, fp8_pages)
+        need = workspace_bytes(a)
+        if need:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = t.empty(need, dtype=t.uint8, device=q.device)
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = workspace.numel() * workspace.element_size()
+        L.check(L.lib().paged_attn_fwd(C.byref(a), t.cuda.current_stream(q.device).cuda_stream), "paged_attn_fwd")
     return out, lse
 
 
@@ -108,7 +110,7 @@ def merge_partials(partial_o, partial_lse, out, lse=None, stream: Optional[int] 
     t = _torch()
     parts, rows, heads, d = partial_o.shape
     dt = _dtype_code(t, out)
-    s = t.cuda.current_stream(out.device).cuda_stream if stream is None else stream
+    s = t.cuda.current_stream(out.device).cuda_stream if stream is None else stream  # allocates nothing
     L.check(L.lib().paged_attn_merge(dt, parts, rows, heads, d, partial_o.data_ptr(), partial_lse.data_ptr(),
                                      out.data_ptr(), _ptr(lse), s), "paged_attn_merge")
     return out, lse

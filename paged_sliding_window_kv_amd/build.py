@@ -42,7 +42,9 @@ def common_flags(debug: bool):
 
 def compile_one(src: str, debug: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    if src.endswith(".hip") or os.path.basename(src) == "api.cpp":
+    with open(src) as f:
+        uses_hip = src.endswith(".hip") or "hip/hip_runtime.h" in f.read()
+    if uses_hip:
         cmd = [_hipcc(), f"--offload-arch={ARCH}", "-x", "hip", src, "-c", "-o", obj,
                # packed fp32 VALU forms are kept out of the generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + common_flags(debug)

@@ -6,8 +6,8 @@ kernels.  PyTorch provides the device memory (the two pools) and the stream.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
-import math
 from typing import Optional, Tuple
 
 import numpy as np
@@ -32,6 +32,20 @@ def torch_dtype(dtype: str):
 def current_stream_ptr(device=None) -> int:
     t = _torch()
     return t.cuda.current_stream(device).cuda_stream
+
+
+def on_stream(stream: Optional[int], device):
+    """Context that makes `stream` (a raw stream pointer) torch's current stream.
+
+    Tensors allocated and copies made inside it are ordered on that stream, the
+    one the library launches on, so the caching allocator does not hand their
+    memory out again while the stream still reads it.  None (or the current
+    stream) changes nothing.
+    """
+    t = _torch()
+    if stream is None or stream == t.cuda.current_stream(device).cuda_stream:
+        return contextlib.nullcontext()
+    return t.cuda.stream(t.cuda.ExternalStream(stream, device=device))
 
 
 class KvCache:
@@ -198,15 +212,30 @@ class KvCache:
         L.check(L.lib().kvc_attend_workspace_size(self._h, num_q, C.byref(n)), "kvc_attend_workspace_size")
         return n.value
 
-    def attend_subset(self, q, keep_ratio: float, seed: int, keep_first: int = 0, keep_last: int = 0, out=None,
-                      lse=None, sm_scale: Optional[float] = None, workspace=None, stream: Optional[int] = None):
-        """Attention of q [Lq, H, d] against a page subset of the visible table (kvc_attend_subset)."""
-        t = _torch()
+    def num_splits(self, num_q: int) -> int:
+        """Key splits an attention call of num_q queries over the current visible table gets (paged_attn_num_splits)."""
+        n = C.c_int32()
+        L.check(L.lib().kvc_build_visible_table(self._h, None, None, 0, C.byref(n), None), "kvc_build_visible_table")
+        a = L.PagedAttnArgs()
+        a.dtype, a.num_heads, a.head_dim, a.page_size = self.cfg.dtype, self.num_heads, self.head_dim, self.page_size
+        a.sm_scale = 1.0
+        a.num_seqs, a.total_q, a.max_qo_len = 1, num_q, num_q
+        a.max_kv_pages, a.num_pool_pages = n.value, self.num_pages
+        out = C.c_int32()
+        L.check(L.lib().paged_attn_num_splits(C.byref(a), C.byref(out)), "paged_attn_num_splits")
+        return out.value
+
+    def _check_q(self, q):
         dev = self.k_pool.device
         if tuple(q.shape) != (q.shape[0], self.num_heads, self.head_dim) or not q.is_contiguous():
             raise ValueError("q must be a contiguous [Lq, H, d] tensor")
         if q.dtype != torch_dtype(self.dtype) or q.device != dev:
             raise ValueError(f"q must be {self.dtype} on {dev}")
+
+    def _outputs(self, q, out, lse, workspace):
+        """out, lse and a workspace of kvc_attend_workspace_size bytes, allocated where missing."""
+        t = _torch()
+        dev = self.k_pool.device
         if out is None:
             out = t.empty_like(q)
         if lse is None:
@@ -216,55 +245,51 @@ class KvCache:
             workspace = t.empty(need, dtype=t.uint8, device=dev)
         wp = workspace.data_ptr() if need else None
         wb = workspace.numel() * workspace.element_size() if need else 0
-        s = current_stream_ptr(dev) if stream is None else stream
-        scale = 0.0 if sm_scale is None else float(sm_scale)
-        L.check(L.lib().kvc_attend_subset(self._h, float(keep_ratio), int(seed) & (2**64 - 1), keep_first, keep_last,
-                                          q.data_ptr(), q.shape[0], scale, out.data_ptr(), lse.data_ptr(), wp, wb, s),
-                "kvc_attend_subset")
+        return out, lse, wp, wb
+
+    def attend_subset(self, q, keep_ratio: float, seed: int, keep_first: int = 0, keep_last: int = 0, out=None,
+                      lse=None, sm_scale: Optional[float] = None, workspace=None, stream: Optional[int] = None):
+        """Attention of q [Lq, H, d] against a page subset of the visible table (kvc_attend_subset)."""
+        self._check_q(q)
+        dev = self.k_pool.device
+        with on_stream(stream, dev):
+            out, lse, wp, wb = self._outputs(q, out, lse, workspace)
+            scale = 0.0 if sm_scale is None else float(sm_scale)
+            L.check(L.lib().kvc_attend_subset(self._h, float(keep_ratio), int(seed) & (2**64 - 1), keep_first,
+                                              keep_last, q.data_ptr(), q.shape[0], scale, out.data_ptr(),
+                                              lse.data_ptr(), wp, wb, current_stream_ptr(dev)), "kvc_attend_subset")
         return out, lse
 
     def attend(self, q, out=None, lse=None, sm_scale: Optional[float] = None, num_splits: int = 0,
                workspace=None, stream: Optional[int] = None):
         """Attention of q [Lq, H, d] against the visible table (one sequence).
 
-        Tables of up to 640 pages travel in the kernel arguments (kvc_attend);
-        longer ones are built on the host, copied to the device and passed to
-        paged_attn_fwd.  num_splits != 0 forces the device-table path with
-        that split count.  Returns (out, lse).
+        kvc_attend builds the table in the library (in the launch arguments up
+        to 640 pages, else staged into the workspace).  num_splits != 0 forces
+        that split count through paged_attn_fwd with a device copy of the
+        table.  Everything is allocated and enqueued on `stream` (default: the
+        current stream).  Returns (out, lse).
         """
-        t = _torch()
+        self._check_q(q)
         dev = self.k_pool.device
-        if out is None:
-            out = t.empty_like(q)
-        if lse is None:
-            lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
-        n = C.c_int32()
-        L.check(L.lib().kvc_build_visible_table(self._h, None, None, 0, C.byref(n), None), "kvc_build_visible_table")
-        if num_splits == 0 and n.value <= L.MAX_INLINE_PAGES:
-            if tuple(q.shape) != (q.shape[0], self.num_heads, self.head_dim) or not q.is_contiguous():
-                raise ValueError("q must be a contiguous [Lq, H, d] tensor")
-            if q.dtype != torch_dtype(self.dtype) or q.device != dev:
-                raise ValueError(f"q must be {self.dtype} on {dev}")
-            need = self.workspace_bytes(q.shape[0])
-            if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-                workspace = t.empty(need, dtype=t.uint8, device=dev)
-            wp = workspace.data_ptr() if need else None
-            wb = workspace.numel() * workspace.element_size() if need else 0
-            s = current_stream_ptr(dev) if stream is None else stream
-            scale = 0.0 if sm_scale is None else float(sm_scale)
-            L.check(L.lib().kvc_attend(self._h, q.data_ptr(), q.shape[0], scale, out.data_ptr(), lse.data_ptr(),
-                                       wp, wb, s), "kvc_attend")
-            return out, lse
-        from .attention import paged_attention
-        ids, lens = self.visible_table()
-        page_ids = t.from_numpy(ids).to(dev)
-        page_lens = t.from_numpy(lens).to(dev)
-        qo = t.tensor([0, q.shape[0]], dtype=t.int32, device=dev)
-        kv = t.tensor([0, len(ids)], dtype=t.int32, device=dev)
-        fp8 = (self.num_pages, self.page_size) if self.dtype == "fp8" else None
-        return paged_attention(q, self.k_pool, self.v_pool, page_ids, page_lens, qo, kv,
-                               max_qo_len=q.shape[0], max_kv_pages=len(ids), out=out, lse=lse,
-                               sm_scale=sm_scale, num_splits=num_splits, stream=stream, fp8_pages=fp8)
+        with on_stream(stream, dev):
+            if num_splits == 0:
+                out, lse, wp, wb = self._outputs(q, out, lse, workspace)
+                scale = 0.0 if sm_scale is None else float(sm_scale)
+                L.check(L.lib().kvc_attend(self._h, q.data_ptr(), q.shape[0], scale, out.data_ptr(),
+                                           lse.data_ptr(), wp, wb, current_stream_ptr(dev)), "kvc_attend")
+                return out, lse
+            from .attention import paged_attention
+            t = _torch()
+            ids, lens = self.visible_table()
+            page_ids = t.from_numpy(ids).to(dev)
+            page_lens = t.from_numpy(lens).to(dev)
+            qo = t.tensor([0, q.shape[0]], dtype=t.int32, device=dev)
+            kv = t.tensor([0, len(ids)], dtype=t.int32, device=dev)
+            fp8 = (self.num_pages, self.page_size) if self.dtype == "fp8" else None
+            return paged_attention(q, self.k_pool, self.v_pool, page_ids, page_lens, qo, kv,
+                                   max_qo_len=q.shape[0], max_kv_pages=len(ids), out=out, lse=lse,
+                                   sm_scale=sm_scale, num_splits=num_splits, fp8_pages=fp8)
 
 
 def shared_pool_caches(count: int, device, **cfg) -> list:
@@ -316,18 +341,19 @@ def attend_batch(caches, q, qo_indptr, out=None, lse=None, sm_scale: Optional[fl
         raise ValueError("q must be a contiguous [total, H, d] tensor")
     if q.dtype != torch_dtype(c0.dtype) or q.device != dev:
         raise ValueError(f"q must be {c0.dtype} on {dev}")
-    if out is None:
-        out = t.empty_like(q)
-    if lse is None:
-        lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
-    need = attend_batch_workspace_bytes(caches, qo)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = t.empty(need, dtype=t.uint8, device=dev)
-    wp = workspace.data_ptr() if need else None
-    wb = workspace.numel() * workspace.element_size() if need else 0
-    s = current_stream_ptr(dev) if stream is None else stream
-    hs = (C.c_void_p * len(caches))(*[c.handle.value for c in caches])
-    scale = 0.0 if sm_scale is None else float(sm_scale)
-    L.check(L.lib().kvc_attend_batch(hs, len(caches), q.data_ptr(), qo.ctypes.data_as(C.POINTER(C.c_int32)), scale,
-                                     out.data_ptr(), lse.data_ptr(), wp, wb, s), "kvc_attend_batch")
+    with on_stream(stream, dev):
+        if out is None:
+            out = t.empty_like(q)
+        if lse is None:
+            lse = t.empty(q.shape[:2], dtype=t.float32, device=dev)
+        need = attend_batch_workspace_bytes(caches, qo)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = t.empty(need, dtype=t.uint8, device=dev)
+        wp = workspace.data_ptr() if need else None
+        wb = workspace.numel() * workspace.element_size() if need else 0
+        hs = (C.c_void_p * len(caches))(*[c.handle.value for c in caches])
+        scale = 0.0 if sm_scale is None else float(sm_scale)
+        L.check(L.lib().kvc_attend_batch(hs, len(caches), q.data_ptr(), qo.ctypes.data_as(C.POINTER(C.c_int32)),
+                                         scale, out.data_ptr(), lse.data_ptr(), wp, wb, current_stream_ptr(dev)),
+                "kvc_attend_batch")
     return out, lse

@@ -1,42 +1,98 @@
 // C ABI of libkvc.so (declared in include/kvc.h).
+//
+// Every extern "C" entry point runs its body inside kvc::guarded(), so no C++
+// exception crosses the boundary; appends plan on the host, launch, and only
+// then commit, so a failed launch leaves the cache as it was.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
-#include <cstdint>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <new>
-#include <string>
 #include <vector>
 
+#include "handle.hpp"
 #include "kernels.hpp"
 #include "kvc.h"
 #include "page_cache.hpp"
 #include "subset.hpp"
 
-struct kvc_cache {
-  kvc::PageCache pc;
-  void* k_pool;
-  void* v_pool;
-  explicit kvc_cache(const kvc_config& c) : pc(c), k_pool(nullptr), v_pool(nullptr) {}
-};
+namespace kvc {
 
 namespace {
+thread_local char g_last_error[512] = "";
+// Measurement hook (kvc_set_kernel_done_event): recorded on the launch stream
+// right after each attention kernel, before the merge of split partials.
+thread_local hipEvent_t g_kernel_done = nullptr;
+}  // namespace
 
-thread_local std::string g_last_error;
-
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int status, const char* fmt, ...) {
-  char buf[512];
+int fail(int status, const char* fmt, ...) noexcept {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return status;
 }
+
+TableRing::~TableRing() {
+  for (int i = 0; i < kSlots; ++i)
+    if (done[i]) {
+      if (in_flight[i]) (void)hipEventSynchronize(done[i]);
+      (void)hipEventDestroy(done[i]);
+    }
+  if (host) (void)hipHostFree(host);
+}
+
+int32_t* TableRing::acquire(size_t words, int* slot) {
+  if (!host || words > slot_words) {
+    // first use, or a longer table than the slots hold: (re)size, after every
+    // copy from the old slots has completed
+    for (int i = 0; i < kSlots; ++i)
+      if (in_flight[i]) {
+        if (hipEventSynchronize(done[i]) != hipSuccess) {
+          fail(KVC_ERR_DEVICE, "table staging: waiting for an earlier copy failed");
+          return nullptr;
+        }
+        in_flight[i] = false;
+      }
+    if (host) (void)hipHostFree(host);
+    host = nullptr;
+    const size_t w = std::max<size_t>(words, 1024);
+    if (hipHostMalloc(reinterpret_cast<void**>(&host), kSlots * w * sizeof(int32_t), hipHostMallocDefault) !=
+        hipSuccess) {
+      host = nullptr;
+      fail(KVC_ERR_DEVICE, "table staging: hipHostMalloc of %zu bytes failed", kSlots * w * sizeof(int32_t));
+      return nullptr;
+    }
+    slot_words = w;
+    for (int i = 0; i < kSlots; ++i)
+      if (!done[i] && hipEventCreateWithFlags(&done[i], hipEventDisableTiming) != hipSuccess) {
+        done[i] = nullptr;
+        fail(KVC_ERR_DEVICE, "table staging: hipEventCreate failed");
+        return nullptr;
+      }
+  }
+  const int s = next;
+  if (in_flight[s]) {
+    if (hipEventSynchronize(done[s]) != hipSuccess) {
+      fail(KVC_ERR_DEVICE, "table staging: waiting for an earlier copy failed");
+      return nullptr;
+    }
+    in_flight[s] = false;
+  }
+  next = (next + 1) % kSlots;
+  *slot = s;
+  return host + static_cast<size_t>(s) * slot_words;
+}
+
+}  // namespace kvc
+
+using kvc::fail;
+using kvc::guarded;
+
+namespace {
 
 size_t elem_size(int dtype) { return dtype == KVC_DTYPE_BF16 ? 2 : dtype == KVC_DTYPE_F32 ? 4 : 1; }
 
@@ -162,171 +218,6 @@ size_t workspace_for(const paged_attn_args& a, int splits) {
   return ((o + 255) & ~size_t(255)) + l;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kvc_strerror(int status) {
-  switch (status) {
-    case KVC_OK: return "ok";
-    case KVC_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case KVC_ERR_OUT_OF_PAGES: return "out of pages";
-    case KVC_ERR_NO_UNDO: return "no append to roll back";
-    case KVC_ERR_BUFFER_TOO_SMALL: return "buffer too small";
-    case KVC_ERR_UNSUPPORTED: return "unsupported";
-    case KVC_ERR_DEVICE: return "device error";
-    default: return "unknown status";
-  }
-}
-
-const char* kvc_last_error(void) { return g_last_error.c_str(); }
-
-int kvc_version(void) { return 100; }
-
-int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages) {
-  if (!cfg || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
-  const int32_t n = kvc::PageCache::required_pages(*cfg);
-  if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
-  *num_pages = n;
-  return KVC_OK;
-}
-
-int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes) {
-  if (!cfg || !bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
-  const int32_t n = cfg->num_pages > 0 ? cfg->num_pages : kvc::PageCache::required_pages(*cfg);
-  if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
-  *bytes = pool_bytes(*cfg, n);
-  return KVC_OK;
-}
-
-int kvc_create(const kvc_config* cfg, void* k_pool, void* v_pool, kvc_t** out) {
-  if (!cfg || !out) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
-  if ((k_pool == nullptr) != (v_pool == nullptr))
-    return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must both be set or both be NULL");
-  if (k_pool && !device_shapes_ok(*cfg))
-    return fail(KVC_ERR_UNSUPPORTED, "device pools need head_dim 64 and page_size a multiple of 64");
-  const int64_t u = (int64_t(cfg->patch_tokens) + cfg->page_size - 1) / cfg->page_size;
-  if (k_pool && u > kvc::kMaxUnitPages)
-    return fail(KVC_ERR_UNSUPPORTED, "a unit spans %lld pages (max %d)", static_cast<long long>(u),
-                kvc::kMaxUnitPages);
-  if (kvc::PageCache::required_pages(*cfg) < 0 && cfg->num_pages == 0)
-    return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
-  kvc_cache* c = new (std::nothrow) kvc_cache(*cfg);
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "out of host memory");
-  c->k_pool = k_pool;
-  c->v_pool = v_pool;
-  *out = c;
-  return KVC_OK;
-}
-
-int kvc_destroy(kvc_t* cache) {
-  delete cache;
-  return KVC_OK;
-}
-
-int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream) {
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  const bool device = c->k_pool != nullptr;
-  if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
-  if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
-  if ((reinterpret_cast<uintptr_t>(k_unit) | reinterpret_cast<uintptr_t>(v_unit)) & 15)
-    return fail(KVC_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
-  kvc::AppendPlan plan;
-  const int s = c->pc.append(device ? &plan : nullptr);
-  if (s != KVC_OK) return fail(s, "append needs %d pages", c->pc.unit_pages());
-  if (!device) return KVC_OK;
-  const kvc_config& cfg = c->pc.config();
-  kvc::AppendParams p{};
-  p.k_src = k_unit;
-  p.v_src = v_unit;
-  p.k_pool = c->k_pool;
-  p.v_pool = c->v_pool;
-  p.num_heads = cfg.num_heads;
-  p.page_size = cfg.page_size;
-  p.patch_tokens = cfg.patch_tokens;
-  p.special_tokens = cfg.special_tokens;
-  p.special_page0 = plan.special_page0;
-  p.special_slot0 = plan.special_slot0;
-  p.special_count0 = plan.special_count0;
-  p.special_page1 = plan.special_page1;
-  p.num_unit_pages = static_cast<int32_t>(plan.unit_pages.size());
-  if (cfg.dtype == KVC_DTYPE_FP8_E4M3) {
-    // row exponents follow the codes in each pool buffer
-    const size_t codes = static_cast<size_t>(c->pc.num_pages()) * cfg.num_heads * cfg.page_size * cfg.head_dim;
-    p.k_exp = static_cast<char*>(c->k_pool) + codes;
-    p.v_exp = static_cast<char*>(c->v_pool) + codes;
-  }
-  std::copy(plan.unit_pages.begin(), plan.unit_pages.end(), p.unit_pages);
-  const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    c->pc.rollback();  // keep the strong guarantee
-    return fail(KVC_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
-  }
-  return KVC_OK;
-}
-
-int kvc_rollback_last_frame(kvc_t* c) {
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  const int s = c->pc.rollback();
-  return s == KVC_OK ? KVC_OK : fail(s, "nothing to roll back");
-}
-
-int kvc_reset(kvc_t* c) {
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  c->pc.reset();
-  return KVC_OK;
-}
-
-int kvc_build_visible_table(const kvc_t* c, int32_t* page_ids, int32_t* page_lens, int32_t capacity,
-                            int32_t* num_pages, int32_t* last_page_len) {
-  if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  const int32_t n = c->pc.visible_count();
-  *num_pages = n;
-  if ((page_ids || page_lens) && capacity < n)
-    return fail(KVC_ERR_BUFFER_TOO_SMALL, "table needs %d entries, capacity %d", n, capacity);
-  if (page_ids && page_lens) {
-    c->pc.visible_table(page_ids, page_lens);
-    if (last_page_len) *last_page_len = n ? page_lens[n - 1] : 0;
-    return KVC_OK;
-  }
-  std::vector<int32_t> ids(n), lens(n);
-  c->pc.visible_table(ids.data(), lens.data());
-  if (page_ids) std::copy(ids.begin(), ids.end(), page_ids);
-  if (page_lens) std::copy(lens.begin(), lens.end(), page_lens);
-  if (last_page_len) *last_page_len = n ? lens[n - 1] : 0;
-  return KVC_OK;
-}
-
-int kvc_get_state(const kvc_t* c, kvc_state* st) {
-  if (!c || !st) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (st->capacity < c->pc.num_pages() &&
-      (st->free_pages || st->scale_pages || st->window_pages || st->special_pages))
-    return fail(KVC_ERR_BUFFER_TOO_SMALL, "state arrays need %d entries", c->pc.num_pages());
-  c->pc.state(st);
-  return KVC_OK;
-}
-
-int paged_attn_workspace_size(const paged_attn_args* a, size_t* bytes) {
-  if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
-  if (int s = check_attn_args(a)) return s;
-  *bytes = workspace_for(*a, max_splits(*a));
-  return KVC_OK;
-}
-
-int paged_attn_num_splits(const paged_attn_args* a, int32_t* num_splits) {
-  if (!num_splits) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL num_splits");
-  if (int s = check_attn_args(a)) return s;
-  *num_splits = choose_splits(*a);
-  return KVC_OK;
-}
-
-}  // extern "C"
-
-namespace {
-
 // Fills the kernel parameters shared by both table sources; returns the
 // split count through *splits_out.
 int setup_attn(const paged_attn_args& a, kvc::AttnParams& p, int* splits_out) {
@@ -381,6 +272,10 @@ int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_
                  : a.dtype == KVC_DTYPE_FP8_E4M3 ? kvc::launch_attn_fp8kv(src, choose_waves(a), st)
                                                  : kvc::launch_attn_f32(src, st);
   if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "attention launch: %s", hipGetErrorString(e));
+  if (kvc::g_kernel_done) {
+    e = hipEventRecord(kvc::g_kernel_done, st);
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "recording the kernel-done event: %s", hipGetErrorString(e));
+  }
   if (splits > 1) {
     // fp32 caches: fp32 partials; bf16 and FP8 caches: fp16 partials, o bf16
     e = a.dtype == KVC_DTYPE_F32
@@ -393,7 +288,7 @@ int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_
   return KVC_OK;
 }
 
-// Attention arguments of one cache-level step (single sequence, table inline).
+// Attention arguments of one cache-level step (single sequence).
 paged_attn_args cache_attn_args(const kvc_t* c, int32_t num_q, int32_t num_entries, float sm_scale) {
   const kvc_config& cfg = c->pc.config();
   paged_attn_args a{};
@@ -413,115 +308,90 @@ paged_attn_args cache_attn_args(const kvc_t* c, int32_t num_q, int32_t num_entri
   return a;
 }
 
-// kvc_attend with an explicit table (ids, lens; n <= kMaxInlinePages
-// entries of this cache's pool): the table travels in the launch arguments.
-int attend_inline(const kvc_t* c, const int32_t* ids, const int32_t* lens, int32_t n, const void* q, int32_t num_q,
-                  float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
+// Whether a table of n entries of cache c can travel in the launch arguments.
+bool inline_table_ok(const kvc_t* c, int32_t n) {
+  return n <= kvc::kMaxInlinePages && c->pc.num_pages() <= kvc::kInlineMaxPid + 1 &&
+         c->pc.config().page_size <= 4095;
+}
+
+// Workspace bytes at its start that hold a device copy of a table of n
+// entries: ids, lens, then the query and entry index pairs of one sequence.
+size_t table_region_bytes(int32_t n) { return (static_cast<size_t>(2 * n + 4) * sizeof(int32_t) + 255) & ~size_t(255); }
+
+// Attention of one cache's queries over an explicit table (ids, lens; n
+// entries of this cache's pool).  Tables of up to 640 entries travel in the
+// launch arguments; longer ones are staged in pinned host memory and copied
+// asynchronously to the start of the workspace on `stream`.
+int attend_table(const kvc_t* c, const int32_t* ids, const int32_t* lens, int32_t n, const void* q, int32_t num_q,
+                 float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
   if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache has no device pools");
   if (num_q < 0 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return fail(KVC_ERR_INVALID_ARGUMENT, "bad num_q or sm_scale");
   if (num_q == 0) return KVC_OK;
   if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
-  if (c->pc.num_pages() > kvc::kInlineMaxPid + 1 || c->pc.config().page_size > 4095)
-    return fail(KVC_ERR_UNSUPPORTED, "pool too large for inline tables");
   paged_attn_args a = cache_attn_args(c, num_q, n, sm_scale);
   a.q = q;
   a.o = o;
   a.lse = lse;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (inline_table_ok(c, n)) {
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    if (int s = check_attn_args(&a)) return s;
+    static thread_local kvc::AttnParamsInline pi;
+    int splits = 1;
+    if (int s = setup_attn(a, pi.base, &splits)) return s;
+    pi.num_entries = n;
+    pi.qo[0] = 0;
+    pi.qo[1] = num_q;
+    pi.kv[0] = 0;
+    pi.kv[1] = n;
+    for (int32_t i = 0; i < n; ++i)
+      pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
+    return launch_attn(a, pi, splits, st);
+  }
+  // device table at the start of the workspace, split partials after it
+  const size_t tb = table_region_bytes(n);
+  if (!workspace || workspace_bytes < tb)
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "a table of %d entries needs a workspace of at least %zu bytes", n, tb);
+  a.workspace = static_cast<char*>(workspace) + tb;
+  a.workspace_bytes = workspace_bytes - tb;
   if (int s = check_attn_args(&a)) return s;
-  static thread_local kvc::AttnParamsInline pi;
-  int splits = 1;
-  if (int s = setup_attn(a, pi.base, &splits)) return s;
-  pi.num_entries = n;
-  pi.qo[0] = 0;
-  pi.qo[1] = num_q;
-  pi.kv[0] = 0;
-  pi.kv[1] = n;
-  for (int32_t i = 0; i < n; ++i)
-    pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
-  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
-}
-
-}  // namespace
-
-extern "C" {
-
-int paged_attn_fwd(const paged_attn_args* a, kvc_stream_t stream) {
-  if (int s = check_attn_args(a)) return s;
-  if (a->num_seqs == 0 || a->total_q == 0 || a->max_qo_len == 0) return KVC_OK;
-  if (!a->qo_indptr || !a->kv_indptr || !a->q || !a->o)
-    return fail(KVC_ERR_INVALID_ARGUMENT, "NULL device pointer");
-  if (a->max_kv_pages > 0 && (!a->page_ids || !a->page_lens || !a->k_pool || !a->v_pool))
-    return fail(KVC_ERR_INVALID_ARGUMENT, "NULL table or pool pointer");
   kvc::AttnParams p;
   int splits = 1;
-  if (int s = setup_attn(*a, p, &splits)) return s;
-  return launch_attn(*a, p, splits, reinterpret_cast<hipStream_t>(stream));
+  if (int s = setup_attn(a, p, &splits)) return s;
+  const size_t words = static_cast<size_t>(2 * n + 4);
+  int slot = 0;
+  int32_t* h = c->ring.acquire(words, &slot);
+  if (!h) return KVC_ERR_DEVICE;
+  std::copy(ids, ids + n, h);
+  std::copy(lens, lens + n, h + n);
+  h[2 * n] = 0;
+  h[2 * n + 1] = num_q;
+  h[2 * n + 2] = 0;
+  h[2 * n + 3] = n;
+  int32_t* d = static_cast<int32_t*>(workspace);
+  hipError_t e = hipMemcpyAsync(d, h, words * sizeof(int32_t), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipEventRecord(c->ring.done[slot], st);
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+  c->ring.in_flight[slot] = true;
+  p.page_ids = d;
+  p.page_lens = d + n;
+  p.qo_indptr = d + 2 * n;
+  p.kv_indptr = d + 2 * n + 2;
+  return launch_attn(a, p, splits, st);
 }
 
-int kvc_attend_workspace_size(const kvc_t* c, int32_t num_q, size_t* bytes) {
-  if (!c || !bytes || num_q < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad argument");
-  const int32_t max_entries = std::min<int32_t>(c->pc.num_pages(), kvc::kMaxInlinePages);
+// Workspace bytes for any attention call of cache c with num_q queries: the
+// split partials of the largest split count its tables can get, plus the
+// device-table region when its tables can outgrow the launch arguments.
+int cache_workspace_bytes(const kvc_t* c, int32_t num_q, size_t* bytes) {
+  const int32_t max_entries = c->pc.num_pages();
   const paged_attn_args a = cache_attn_args(c, num_q, max_entries, 0.f);
   if (int s = check_attn_args(&a)) return s;
-  *bytes = workspace_for(a, max_splits(a));
+  *bytes = workspace_for(a, max_splits(a)) + (inline_table_ok(c, max_entries) ? 0 : table_region_bytes(max_entries));
   return KVC_OK;
 }
-
-int kvc_attend(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
-               void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  const int32_t n = c->pc.visible_count();
-  if (n > kvc::kMaxInlinePages)
-    return fail(KVC_ERR_UNSUPPORTED, "visible table has %d pages; kvc_attend passes at most %d (use paged_attn_fwd)",
-                n, kvc::kMaxInlinePages);
-  int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
-  c->pc.visible_table(ids, lens);
-  return attend_inline(c, ids, lens, n, q, num_q, sm_scale, o, lse, workspace, workspace_bytes, stream);
-}
-
-int kvc_build_subset_table(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
-                           int32_t* page_ids, int32_t* page_lens, int32_t capacity, int32_t* num_pages) {
-  if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
-  if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
-  const int32_t n = c->pc.visible_count();
-  std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
-  c->pc.visible_table(ids.data(), lens.data());
-  std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
-  const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last, sid.data(),
-                                       slen.data());
-  *num_pages = m;
-  if (capacity < m || (m > 0 && (!page_ids || !page_lens)))
-    return fail(KVC_ERR_BUFFER_TOO_SMALL, "subset table needs %d entries", m);
-  std::copy(sid.begin(), sid.begin() + m, page_ids);
-  std::copy(slen.begin(), slen.begin() + m, page_lens);
-  return KVC_OK;
-}
-
-int kvc_attend_subset(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
-                      const void* q, int32_t num_q, float sm_scale, void* o, float* lse, void* workspace,
-                      size_t workspace_bytes, kvc_stream_t stream) {
-  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-  if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
-  if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
-  const int32_t n = c->pc.visible_count();
-  std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
-  c->pc.visible_table(ids.data(), lens.data());
-  std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
-  const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last,
-                                       sid.data(), slen.data());
-  if (m > kvc::kMaxInlinePages)
-    return fail(KVC_ERR_UNSUPPORTED, "subset table has %d pages; at most %d travel inline (use paged_attn_fwd)", m,
-                kvc::kMaxInlinePages);
-  return attend_inline(c, sid.data(), slen.data(), m, q, num_q, sm_scale, o, lse, workspace, workspace_bytes, stream);
-}
-
-}  // extern "C"
-
-namespace {
 
 // Checks a batch of caches for kvc_attend_batch and derives its launch
 // arguments: every cache's pool offset (whole pages from the lowest pool
@@ -596,64 +466,335 @@ int batch_args(const kvc_t* const* caches, int32_t n, const int32_t* qo, float s
 
 extern "C" {
 
+const char* kvc_strerror(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KVC_ERR_OUT_OF_PAGES: return "out of pages";
+    case KVC_ERR_NO_UNDO: return "no append to roll back";
+    case KVC_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case KVC_ERR_UNSUPPORTED: return "unsupported";
+    case KVC_ERR_DEVICE: return "device error";
+    case KVC_ERR_HOST_MEMORY: return "out of host memory";
+    case KVC_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvc_last_error(void) { return kvc::g_last_error; }
+
+int kvc_version(void) { return 200; }
+
+int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages) {
+  return guarded("kvc_required_pages", [&] {
+    if (!cfg || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+    const int32_t n = kvc::PageCache::required_pages(*cfg);
+    if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+    *num_pages = n;
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_pool_bytes(const kvc_config* cfg, size_t* bytes) {
+  return guarded("kvc_pool_bytes", [&] {
+    if (!cfg || !bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+    const int32_t n = cfg->num_pages > 0 ? cfg->num_pages : kvc::PageCache::required_pages(*cfg);
+    if (n < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+    *bytes = pool_bytes(*cfg, n);
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_create(const kvc_config* cfg, void* k_pool, void* v_pool, kvc_t** out) {
+  return guarded("kvc_create", [&] {
+    if (!cfg || !out) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (int s = kvc::PageCache::validate(*cfg)) return fail(s, "invalid kvc_config");
+    if ((k_pool == nullptr) != (v_pool == nullptr))
+      return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must both be set or both be NULL");
+    if (k_pool && !device_shapes_ok(*cfg))
+      return fail(KVC_ERR_UNSUPPORTED, "device pools need head_dim 64 and page_size a multiple of 64");
+    const int64_t u = (int64_t(cfg->patch_tokens) + cfg->page_size - 1) / cfg->page_size;
+    if (k_pool && u > kvc::kMaxUnitPages)
+      return fail(KVC_ERR_UNSUPPORTED, "a unit spans %lld pages (max %d)", static_cast<long long>(u),
+                  kvc::kMaxUnitPages);
+    if (kvc::PageCache::required_pages(*cfg) < 0 && cfg->num_pages == 0)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "page count overflows int32");
+    kvc_cache* c = new kvc_cache(*cfg);  // bad_alloc -> KVC_ERR_HOST_MEMORY
+    c->k_pool = k_pool;
+    c->v_pool = v_pool;
+    *out = c;
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_destroy(kvc_t* cache) {
+  return guarded("kvc_destroy", [&] {
+    delete cache;
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream) {
+  return guarded("kvc_append_frame", [&] {
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+    const bool device = c->k_pool != nullptr;
+    if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
+    if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
+    if ((reinterpret_cast<uintptr_t>(k_unit) | reinterpret_cast<uintptr_t>(v_unit)) & 15)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
+    if (!device) {
+      const int s = c->pc.append();
+      return s == KVC_OK ? s : fail(s, "append needs %d pages", c->pc.unit_pages());
+    }
+    // plan, launch, then commit: a failed launch leaves the cache unchanged
+    kvc::AppendPlan plan;
+    kvc::AppendParams p{};
+    if (int s = c->pc.plan(&plan, p.unit_pages)) return fail(s, "append needs %d pages", c->pc.unit_pages());
+    const kvc_config& cfg = c->pc.config();
+    p.k_src = k_unit;
+    p.v_src = v_unit;
+    p.k_pool = c->k_pool;
+    p.v_pool = c->v_pool;
+    p.num_heads = cfg.num_heads;
+    p.page_size = cfg.page_size;
+    p.patch_tokens = cfg.patch_tokens;
+    p.special_tokens = cfg.special_tokens;
+    p.special_page0 = plan.special_page0;
+    p.special_slot0 = plan.special_slot0;
+    p.special_count0 = plan.special_count0;
+    p.special_page1 = plan.special_page1;
+    p.num_unit_pages = plan.num_unit_pages;
+    if (cfg.dtype == KVC_DTYPE_FP8_E4M3) {
+      // row exponents follow the codes in each pool buffer
+      const size_t codes = static_cast<size_t>(c->pc.num_pages()) * cfg.num_heads * cfg.page_size * cfg.head_dim;
+      p.k_exp = static_cast<char*>(c->k_pool) + codes;
+      p.v_exp = static_cast<char*>(c->v_pool) + codes;
+    }
+    const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+    c->pc.commit();
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_rollback_last_frame(kvc_t* c) {
+  return guarded("kvc_rollback_last_frame", [&] {
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+    const int s = c->pc.rollback();
+    return s == KVC_OK ? s : fail(s, "nothing to roll back");
+  });
+}
+
+int kvc_reset(kvc_t* c) {
+  return guarded("kvc_reset", [&] {
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+    c->pc.reset();
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_build_visible_table(const kvc_t* c, int32_t* page_ids, int32_t* page_lens, int32_t capacity,
+                            int32_t* num_pages, int32_t* last_page_len) {
+  return guarded("kvc_build_visible_table", [&] {
+    if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    const int32_t n = c->pc.visible_count();
+    *num_pages = n;
+    if ((page_ids || page_lens) && capacity < n)
+      return fail(KVC_ERR_BUFFER_TOO_SMALL, "table needs %d entries, capacity %d", n, capacity);
+    if (page_ids || page_lens) c->pc.visible_table(page_ids, page_lens);
+    if (last_page_len) {
+      // the last entry's length, read without a caller array when none was given
+      if (page_lens) {
+        *last_page_len = n ? page_lens[n - 1] : 0;
+      } else {
+        std::vector<int32_t> lens(static_cast<size_t>(n));
+        c->pc.visible_table(nullptr, lens.data());
+        *last_page_len = n ? lens[n - 1] : 0;
+      }
+    }
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_get_state(const kvc_t* c, kvc_state* st) {
+  return guarded("kvc_get_state", [&] {
+    if (!c || !st) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (st->capacity < c->pc.num_pages() &&
+        (st->free_pages || st->scale_pages || st->window_pages || st->special_pages))
+      return fail(KVC_ERR_BUFFER_TOO_SMALL, "state arrays need %d entries", c->pc.num_pages());
+    c->pc.state(st);
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int paged_attn_workspace_size(const paged_attn_args* a, size_t* bytes) {
+  return guarded("paged_attn_workspace_size", [&] {
+    if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
+    if (int s = check_attn_args(a)) return s;
+    *bytes = workspace_for(*a, max_splits(*a));
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int paged_attn_num_splits(const paged_attn_args* a, int32_t* num_splits) {
+  return guarded("paged_attn_num_splits", [&] {
+    if (!num_splits) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL num_splits");
+    if (int s = check_attn_args(a)) return s;
+    *num_splits = choose_splits(*a);
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int paged_attn_fwd(const paged_attn_args* a, kvc_stream_t stream) {
+  return guarded("paged_attn_fwd", [&] {
+    if (int s = check_attn_args(a)) return s;
+    if (a->num_seqs == 0 || a->total_q == 0 || a->max_qo_len == 0) return static_cast<int>(KVC_OK);
+    if (!a->qo_indptr || !a->kv_indptr || !a->q || !a->o)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (a->max_kv_pages > 0 && (!a->page_ids || !a->page_lens || !a->k_pool || !a->v_pool))
+      return fail(KVC_ERR_INVALID_ARGUMENT, "NULL table or pool pointer");
+    kvc::AttnParams p;
+    int splits = 1;
+    if (int s = setup_attn(*a, p, &splits)) return s;
+    return launch_attn(*a, p, splits, reinterpret_cast<hipStream_t>(stream));
+  });
+}
+
+int kvc_attend_workspace_size(const kvc_t* c, int32_t num_q, size_t* bytes) {
+  return guarded("kvc_attend_workspace_size", [&] {
+    if (!c || !bytes || num_q < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad argument");
+    return cache_workspace_bytes(c, num_q, bytes);
+  });
+}
+
+int kvc_attend(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
+  return guarded("kvc_attend", [&] {
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+    const int32_t n = c->pc.visible_count();
+    if (n <= kvc::kMaxInlinePages) {
+      int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
+      c->pc.visible_table(ids, lens);
+      return attend_table(c, ids, lens, n, q, num_q, sm_scale, o, lse, workspace, workspace_bytes, stream);
+    }
+    std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
+    c->pc.visible_table(ids.data(), lens.data());
+    return attend_table(c, ids.data(), lens.data(), n, q, num_q, sm_scale, o, lse, workspace, workspace_bytes,
+                        stream);
+  });
+}
+
+int kvc_build_subset_table(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
+                           int32_t* page_ids, int32_t* page_lens, int32_t capacity, int32_t* num_pages) {
+  return guarded("kvc_build_subset_table", [&] {
+    if (!c || !num_pages) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
+    if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
+    const int32_t n = c->pc.visible_count();
+    std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
+    c->pc.visible_table(ids.data(), lens.data());
+    std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
+    const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last,
+                                         sid.data(), slen.data());
+    *num_pages = m;
+    if (capacity < m || (m > 0 && (!page_ids || !page_lens)))
+      return fail(KVC_ERR_BUFFER_TOO_SMALL, "subset table needs %d entries", m);
+    std::copy(sid.begin(), sid.begin() + m, page_ids);
+    std::copy(slen.begin(), slen.begin() + m, page_lens);
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_attend_subset(const kvc_t* c, float keep_ratio, uint64_t seed, int32_t keep_first, int32_t keep_last,
+                      const void* q, int32_t num_q, float sm_scale, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, kvc_stream_t stream) {
+  return guarded("kvc_attend_subset", [&] {
+    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+    if (!(keep_ratio > 0.f && keep_ratio <= 1.f)) return fail(KVC_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1]");
+    if (keep_first < 0 || keep_last < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "negative keep_first/keep_last");
+    const int32_t n = c->pc.visible_count();
+    std::vector<int32_t> ids(static_cast<size_t>(n)), lens(static_cast<size_t>(n));
+    c->pc.visible_table(ids.data(), lens.data());
+    std::vector<int32_t> sid(static_cast<size_t>(n)), slen(static_cast<size_t>(n));
+    const int32_t m = kvc::subset_select(ids.data(), lens.data(), n, keep_ratio, seed, keep_first, keep_last,
+                                         sid.data(), slen.data());
+    return attend_table(c, sid.data(), slen.data(), m, q, num_q, sm_scale, o, lse, workspace, workspace_bytes,
+                        stream);
+  });
+}
+
 int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_caches, const int32_t* qo_indptr,
                                     size_t* bytes) {
-  if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
-  paged_attn_args a;
-  int32_t off[kvc::kMaxInlineSeqs];
-  if (int s = batch_args(caches, num_caches, qo_indptr, 0.f, &a, off)) return s;
-  if (int s = check_attn_args(&a)) return s;
-  *bytes = workspace_for(a, max_splits(a));
-  return KVC_OK;
+  return guarded("kvc_attend_batch_workspace_size", [&] {
+    if (!bytes) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL bytes");
+    paged_attn_args a;
+    int32_t off[kvc::kMaxInlineSeqs];
+    if (int s = batch_args(caches, num_caches, qo_indptr, 0.f, &a, off)) return s;
+    if (int s = check_attn_args(&a)) return s;
+    *bytes = workspace_for(a, max_splits(a));
+    return static_cast<int>(KVC_OK);
+  });
 }
 
 int kvc_attend_batch(const kvc_t* const* caches, int32_t num_caches, const void* q, const int32_t* qo_indptr,
                      float sm_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
                      kvc_stream_t stream) {
-  paged_attn_args a;
-  int32_t off[kvc::kMaxInlineSeqs];
-  if (int s = batch_args(caches, num_caches, qo_indptr, sm_scale, &a, off)) return s;
-  if (a.total_q == 0) return KVC_OK;
-  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
-  a.q = q;
-  a.o = o;
-  a.lse = lse;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
-  if (int s = check_attn_args(&a)) return s;
-  static thread_local kvc::AttnParamsInline pi;
-  int splits = 1;
-  if (int s = setup_attn(a, pi.base, &splits)) return s;
-  int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
-  int32_t e = 0;
-  pi.qo[0] = 0;
-  pi.kv[0] = 0;
-  for (int32_t i = 0; i < num_caches; ++i) {
-    const int32_t m = caches[i]->pc.visible_count();
-    caches[i]->pc.visible_table(ids + e, lens + e);
-    for (int32_t j = e; j < e + m; ++j)
-      pi.entries[j] = static_cast<uint32_t>(ids[j] + off[i]) | (static_cast<uint32_t>(lens[j]) << kvc::kInlinePidBits);
-    e += m;
-    pi.qo[i + 1] = qo_indptr[i + 1];
-    pi.kv[i + 1] = e;
-  }
-  pi.num_entries = e;
-  return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
+  return guarded("kvc_attend_batch", [&] {
+    paged_attn_args a;
+    int32_t off[kvc::kMaxInlineSeqs];
+    if (int s = batch_args(caches, num_caches, qo_indptr, sm_scale, &a, off)) return s;
+    if (a.total_q == 0) return static_cast<int>(KVC_OK);
+    if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
+    a.q = q;
+    a.o = o;
+    a.lse = lse;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    if (int s = check_attn_args(&a)) return s;
+    static thread_local kvc::AttnParamsInline pi;
+    int splits = 1;
+    if (int s = setup_attn(a, pi.base, &splits)) return s;
+    int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
+    int32_t e = 0;
+    pi.qo[0] = 0;
+    pi.kv[0] = 0;
+    for (int32_t i = 0; i < num_caches; ++i) {
+      const int32_t m = caches[i]->pc.visible_count();
+      caches[i]->pc.visible_table(ids + e, lens + e);
+      for (int32_t j = e; j < e + m; ++j)
+        pi.entries[j] =
+            static_cast<uint32_t>(ids[j] + off[i]) | (static_cast<uint32_t>(lens[j]) << kvc::kInlinePidBits);
+      e += m;
+      pi.qo[i + 1] = qo_indptr[i + 1];
+      pi.kv[i + 1] = e;
+    }
+    pi.num_entries = e;
+    return launch_attn(a, pi, splits, reinterpret_cast<hipStream_t>(stream));
+  });
 }
 
 int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num_heads, int32_t head_dim,
                      const float* partial_o, const float* partial_lse, void* o, float* lse, kvc_stream_t stream) {
-  if (dtype != KVC_DTYPE_BF16 && dtype != KVC_DTYPE_F32) return fail(KVC_ERR_INVALID_ARGUMENT, "bad dtype");
-  if (head_dim != kvc::kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "head_dim %d (need 64)", head_dim);
-  if (num_parts <= 0 || rows < 0 || num_heads <= 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad sizes");
-  if (rows == 0) return KVC_OK;
-  if (!partial_o || !partial_lse || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL pointer");
-  // the merge reads partial O and writes O in 16- and 8-byte vectors
-  if ((reinterpret_cast<uintptr_t>(partial_o) & 15) || (reinterpret_cast<uintptr_t>(o) & 15))
-    return fail(KVC_ERR_INVALID_ARGUMENT, "partial_o and o must be 16-byte aligned");
-  const hipError_t e = kvc::launch_attn_merge(dtype, num_parts, rows, num_heads, partial_o, partial_lse, o, lse,
-                                              reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  return guarded("paged_attn_merge", [&] {
+    if (dtype != KVC_DTYPE_BF16 && dtype != KVC_DTYPE_F32) return fail(KVC_ERR_INVALID_ARGUMENT, "bad dtype");
+    if (head_dim != kvc::kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "head_dim %d (need 64)", head_dim);
+    if (num_parts <= 0 || rows < 0 || num_heads <= 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad sizes");
+    if (rows == 0) return static_cast<int>(KVC_OK);
+    if (!partial_o || !partial_lse || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL pointer");
+    // the merge reads partial O and writes O in 16- and 8-byte vectors
+    if ((reinterpret_cast<uintptr_t>(partial_o) & 15) || (reinterpret_cast<uintptr_t>(o) & 15))
+      return fail(KVC_ERR_INVALID_ARGUMENT, "partial_o and o must be 16-byte aligned");
+    const hipError_t e = kvc::launch_attn_merge(dtype, num_parts, rows, num_heads, partial_o, partial_lse, o, lse,
+                                                reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_set_kernel_done_event(void* event) {
+  kvc::g_kernel_done = static_cast<hipEvent_t>(event);
   return KVC_OK;
 }
 

@@ -265,9 +265,8 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
   floatx4* const lds_xo = reinterpret_cast<floatx4*>(smem + RING_BYTES + Q_BYTES);  // [wave][db][lane]
 
   // ---- which (sequence, head, split, query tile) ----------------------------
-  const int L = blockIdx.x;
-  const int g = L % p.groups_padded;
-  const int qt = L / p.groups_padded;
+  int g, qt;
+  attn_tile_of(p, blockIdx.x, g, qt);
   if (g >= p.groups) return;
   const int split = g % p.num_splits;
   const int sh = g / p.num_splits;
@@ -901,9 +900,8 @@ __global__ __launch_bounds__(512) void attn_pipe_kernel(const Src src) {
   const AttnParams& p = attn_base(src);
 
   // ---- which (sequence, head, split, query tile): as attn_bf16_kernel -----
-  const int L = blockIdx.x;
-  const int g = L % p.groups_padded;
-  const int qt = L / p.groups_padded;
+  int g, qt;
+  attn_tile_of(p, blockIdx.x, g, qt);
   if (g >= p.groups) return;
   const int split = g % p.num_splits;
   const int sh = g / p.num_splits;
@@ -1323,9 +1321,8 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
   const AttnParams& p = attn_base(src);
 
   // ---- which (sequence, head, split, query tile): as attn_bf16_kernel -----
-  const int L = blockIdx.x;
-  const int g = L % p.groups_padded;
-  const int qt = L / p.groups_padded;
+  int g, qt;
+  attn_tile_of(p, blockIdx.x, g, qt);
   if (g >= p.groups) return;
   const int split = g % p.num_splits;
   const int sh = g / p.num_splits;

@@ -94,14 +94,13 @@ __device__ __forceinline__ void cursor_advance(const Src& src, int ee, TileCurso
 }
 
 template <class Src>
-__global__ __launch_bounds__(NT, 2) void attn_f32_kernel(const Src src) {
+__global__ __launch_bounds__(NT) void attn_f32_kernel(const Src src) {
   const AttnParams& p = attn_base(src);
   __shared__ __attribute__((aligned(16))) float lds[2][2][TILE];  // [buffer][K, V^T][row * 64 + dim or key]
 
   // ---- which (sequence, head, split, query tile) --------------------------
-  const int L = blockIdx.x;
-  const int g = L % p.groups_padded;
-  const int qt = L / p.groups_padded;
+  int g, qt;
+  attn_tile_of(p, blockIdx.x, g, qt);
   if (g >= p.groups) return;
   const int split = g % p.num_splits;
   const int sh = g / p.num_splits;

@@ -116,6 +116,20 @@ __device__ __forceinline__ void attn_seq(const AttnParamsInline& p, int seq, int
   en = p.kv[seq + 1] - e0;
 }
 
+// Workgroup index -> (group, query tile).  The dispatcher hands workgroups to
+// the eight XCDs round-robin by index, so XCD x runs indices x, x+8, x+16, ...
+// The i-th of those takes query tile i % q_tiles of group 8 * (i / q_tiles) + x:
+// all query tiles of one (sequence, head, split) group run on one XCD, one
+// after the other, so the workgroups an XCD holds at a time read the key
+// ranges of one or two groups, which its L2 then serves to all of them.
+// groups_padded (a multiple of 8) times q_tiles workgroups cover every pair;
+// groups at or past p.groups are padding.
+__device__ __forceinline__ void attn_tile_of(const AttnParams& p, int wg, int& g, int& qt) {
+  const int x = wg & 7, i = wg >> 3;
+  qt = i % p.q_tiles;
+  g = (i / p.q_tiles) * 8 + x;
+}
+
 // Page id and valid length of table entry e; invalid ids and lengths give 0.
 __device__ __forceinline__ void attn_entry(const AttnParams& p, int e, int& pid, int& len) {
   pid = ld_const(p.page_ids, e);

@@ -2,6 +2,7 @@
 #include "page_cache.hpp"
 
 #include <algorithm>
+#include <climits>
 
 namespace kvc {
 
@@ -37,6 +38,18 @@ PageCache::PageCache(const kvc_config& cfg) : cfg_(cfg) {
   unit_pages_ = ceil_div(cfg.patch_tokens, cfg.page_size);
   unit_tail_ = cfg.patch_tokens - cfg.page_size * (unit_pages_ - 1);
   num_pages_ = cfg.num_pages > 0 ? cfg.num_pages : required_pages(cfg);
+  // Every unit holds unit_pages_ pool pages, so at most num_pages_ / unit_pages_
+  // units exist at once; the window ring needs one slot more than the window
+  // holds (an append pushes before it evicts, and a rollback finds the evicted
+  // unit still in its slot).
+  const int32_t most_units = num_pages_ / unit_pages_;
+  const int32_t scale_units = std::min(cfg.num_scale_units, most_units);
+  win_cap_ = most_units + 1;
+  if (cfg.window_units > 0) win_cap_ = std::min(win_cap_, cfg.window_units + 1);
+  free_.reserve(num_pages_);
+  scale_.reserve(static_cast<size_t>(scale_units) * unit_pages_);
+  win_.assign(static_cast<size_t>(win_cap_) * unit_pages_, -1);
+  special_.reserve(num_pages_);
   reset();
 }
 
@@ -44,12 +57,15 @@ void PageCache::reset() {
   free_.resize(num_pages_);
   for (int32_t i = 0; i < num_pages_; ++i) free_[i] = num_pages_ - 1 - i;  // pops give 0, 1, 2, ...
   scale_.clear();
-  window_.clear();
+  win_head_ = 0;
+  win_count_ = 0;
   special_.clear();
   fill_ = 0;
   n_ = 0;
   has_undo_ = false;
-  undo_ = Undo{};
+  undo_to_scale_ = undo_evicted_ = false;
+  undo_special_ = -1;
+  undo_prev_fill_ = 0;
 }
 
 int32_t PageCache::frames_per_special_page() const {
@@ -61,126 +77,155 @@ int32_t PageCache::full_special_len() const {
                                                           : cfg_.page_size;
 }
 
-int PageCache::append(AppendPlan* plan) {
+// Does the next unit's special tokens need a fresh special page?  Frame
+// aligned: when there is none yet or the last one holds its whole frames;
+// contiguous: when the last one has less room than one unit's tokens.
+bool PageCache::needs_special_page() const {
   const int32_t x = cfg_.special_tokens;
-  const int32_t page = cfg_.page_size;
-  // Where do this unit's special tokens go, and is a new special page needed?
-  bool open_special = false;
-  int32_t slot0 = 0, count0 = 0;
-  if (x > 0) {
-    if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED) {
-      open_special = special_.empty() || fill_ == frames_per_special_page();
-      slot0 = open_special ? 0 : x * fill_;
-      count0 = x;
-    } else {
-      const int32_t room = special_.empty() ? 0 : page - fill_;
-      open_special = room < x;
-      count0 = std::min(room, x);
-      slot0 = special_.empty() ? 0 : fill_;
-    }
-  }
+  if (x == 0) return false;
+  if (special_.empty()) return true;
+  if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED) return fill_ == frames_per_special_page();
+  return cfg_.page_size - fill_ < x;
+}
+
+int PageCache::plan(AppendPlan* plan, int32_t* unit_pages) const {
+  const int32_t x = cfg_.special_tokens;
+  const bool open_special = needs_special_page();
   const int32_t need = unit_pages_ + (open_special ? 1 : 0);
   if (static_cast<int32_t>(free_.size()) < need) return KVC_ERR_OUT_OF_PAGES;
-
-  // Patch pages first, then the special page.
-  std::vector<int32_t> unit(unit_pages_);
-  for (int32_t i = 0; i < unit_pages_; ++i) {
-    unit[i] = free_.back();
-    free_.pop_back();
-  }
-  Undo ud;
-  ud.prev_fill = fill_;
-  if (open_special) {
-    ud.new_special = free_.back();
-    free_.pop_back();
-    special_.push_back(ud.new_special);
-  }
-  if (plan) {
-    plan->unit_pages = unit;
-    plan->special_page0 = plan->special_page1 = -1;
-    plan->special_slot0 = plan->special_count0 = 0;
-    if (x > 0) {
-      if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED) {
-        plan->special_page0 = special_.back();
-        plan->special_slot0 = slot0;
-        plan->special_count0 = x;
-      } else if (count0 > 0) {
-        const size_t cur = special_.size() - (open_special ? 2 : 1);
-        plan->special_page0 = special_[cur];
-        plan->special_slot0 = slot0;
-        plan->special_count0 = count0;
-        if (open_special) plan->special_page1 = special_.back();
-      } else {
-        plan->special_page0 = special_.back();
-        plan->special_slot0 = 0;
-        plan->special_count0 = x;
-      }
+  // Patch pages are popped first, then the special page.
+  const size_t top = free_.size() - 1;
+  if (unit_pages)
+    for (int32_t i = 0; i < unit_pages_; ++i) unit_pages[i] = free_[top - i];
+  const int32_t new_special = open_special ? free_[top - unit_pages_] : -1;
+  if (!plan) return KVC_OK;
+  *plan = AppendPlan{};
+  plan->num_unit_pages = unit_pages_;
+  if (x == 0) return KVC_OK;
+  if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED) {
+    // a unit's tokens never straddle: a fresh page, or the next whole-frame slot
+    plan->special_page0 = open_special ? new_special : special_.back();
+    plan->special_slot0 = open_special ? 0 : x * fill_;
+    plan->special_count0 = x;
+  } else {
+    // the room left in the last page first, the rest at the start of a fresh page
+    const int32_t room = special_.empty() ? 0 : cfg_.page_size - fill_;
+    const int32_t count0 = std::min(room, x);
+    if (count0 > 0) {
+      plan->special_page0 = special_.back();
+      plan->special_slot0 = fill_;
+      plan->special_count0 = count0;
+      if (open_special) plan->special_page1 = new_special;
+    } else {
+      plan->special_page0 = new_special;
+      plan->special_slot0 = 0;
+      plan->special_count0 = x;
     }
+  }
+  return KVC_OK;
+}
+
+void PageCache::commit() {
+  const int32_t x = cfg_.special_tokens;
+  const bool open_special = needs_special_page();
+  const int32_t room = special_.empty() ? 0 : cfg_.page_size - fill_;  // contiguous packing
+  undo_prev_fill_ = fill_;
+  undo_special_ = -1;
+  undo_evicted_ = false;
+  undo_to_scale_ = n_ < cfg_.num_scale_units;
+  // Pop the unit's pages straight into their stream.
+  int32_t* dst;
+  if (undo_to_scale_) {
+    const size_t at = scale_.size();
+    scale_.resize(at + unit_pages_);  // within the reserved capacity
+    dst = scale_.data() + at;
+  } else {
+    dst = window_slot(win_count_);
+    ++win_count_;
+  }
+  for (int32_t i = 0; i < unit_pages_; ++i) {
+    dst[i] = free_.back();
+    free_.pop_back();
+  }
+  if (open_special) {
+    undo_special_ = free_.back();
+    free_.pop_back();
+    special_.push_back(undo_special_);
   }
   if (x > 0) {
-    if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED)
+    if (cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED) {
       fill_ = open_special ? 1 : fill_ + 1;
-    else
-      fill_ = open_special ? x - count0 : fill_ + x;
-  }
-  ud.to_scale = n_ < cfg_.num_scale_units;
-  if (ud.to_scale) {
-    scale_.push_back(unit);
-  } else {
-    window_.push_back(unit);
-    if (cfg_.window_units > 0 && static_cast<int32_t>(window_.size()) > cfg_.window_units) {
-      ud.evicted = std::move(window_.front());
-      ud.has_evicted = true;
-      window_.pop_front();
-      for (auto it = ud.evicted.rbegin(); it != ud.evicted.rend(); ++it) free_.push_back(*it);
+    } else {
+      // contiguous: the tokens that did not fit the old page start the new one
+      fill_ = open_special ? x - std::min(room, x) : fill_ + x;
     }
   }
-  ud.unit = std::move(unit);
-  undo_ = std::move(ud);
+  // After all pops: evict the oldest window unit beyond the window, pushing
+  // its pages in reverse so that a later pop returns its first page first.
+  if (!undo_to_scale_ && cfg_.window_units > 0 && win_count_ > cfg_.window_units) {
+    const int32_t* e = window_unit(0);
+    for (int32_t i = unit_pages_ - 1; i >= 0; --i) free_.push_back(e[i]);
+    win_head_ = (win_head_ + 1) % win_cap_;
+    --win_count_;
+    undo_evicted_ = true;
+  }
   has_undo_ = true;
   ++n_;
+}
+
+int PageCache::append() {
+  if (int s = plan(nullptr, nullptr)) return s;
+  commit();
   return KVC_OK;
 }
 
 int PageCache::rollback() {
   if (!has_undo_) return KVC_ERR_NO_UNDO;
-  Undo& ud = undo_;
-  if (ud.has_evicted) {
-    // The evicted pages sit on top of the free stack in pop order.
-    free_.resize(free_.size() - ud.evicted.size());
-    window_.push_front(std::move(ud.evicted));
+  if (undo_evicted_) {
+    // The evicted pages sit on top of the free stack in pop order, and the
+    // unit is still in the ring slot before the head.
+    free_.resize(free_.size() - unit_pages_);
+    win_head_ = (win_head_ + win_cap_ - 1) % win_cap_;
+    ++win_count_;
   }
-  if (ud.new_special >= 0) {
+  if (undo_special_ >= 0) {
     special_.pop_back();
-    free_.push_back(ud.new_special);
+    free_.push_back(undo_special_);
   }
-  fill_ = ud.prev_fill;
+  fill_ = undo_prev_fill_;
   --n_;
-  if (ud.to_scale)
-    scale_.pop_back();
+  const int32_t* u;
+  if (undo_to_scale_) {
+    u = scale_.data() + scale_.size() - unit_pages_;
+  } else {
+    u = window_unit(win_count_ - 1);
+  }
+  for (int32_t i = unit_pages_ - 1; i >= 0; --i) free_.push_back(u[i]);
+  if (undo_to_scale_)
+    scale_.resize(scale_.size() - unit_pages_);
   else
-    window_.pop_back();
-  for (auto it = ud.unit.rbegin(); it != ud.unit.rend(); ++it) free_.push_back(*it);
+    --win_count_;
   has_undo_ = false;
-  undo_ = Undo{};
+  undo_to_scale_ = undo_evicted_ = false;
+  undo_special_ = -1;
   return KVC_OK;
 }
 
 int32_t PageCache::visible_count() const {
-  return static_cast<int32_t>((scale_.size() + window_.size()) * unit_pages_ + special_.size());
+  return static_cast<int32_t>(scale_.size()) + win_count_ * unit_pages_ + static_cast<int32_t>(special_.size());
 }
 
 void PageCache::visible_table(int32_t* ids, int32_t* lens) const {
   int32_t k = 0;
-  auto put_unit = [&](const std::vector<int32_t>& u) {
+  auto put_unit = [&](const int32_t* u) {
     for (int32_t i = 0; i < unit_pages_; ++i) {
       if (ids) ids[k] = u[i];
       if (lens) lens[k] = (i == unit_pages_ - 1) ? unit_tail_ : cfg_.page_size;
       ++k;
     }
   };
-  for (const auto& u : scale_) put_unit(u);
-  for (const auto& u : window_) put_unit(u);
+  for (size_t i = 0; i < scale_.size(); i += unit_pages_) put_unit(scale_.data() + i);
+  for (int32_t i = 0; i < win_count_; ++i) put_unit(window_unit(i));
   const int32_t full = full_special_len();
   const int32_t last = cfg_.special_packing == KVC_SPECIAL_FRAME_ALIGNED ? cfg_.special_tokens * fill_ : fill_;
   for (size_t i = 0; i < special_.size(); ++i) {
@@ -192,24 +237,22 @@ void PageCache::visible_table(int32_t* ids, int32_t* lens) const {
 
 void PageCache::state(kvc_state* st) const {
   st->num_free = static_cast<int32_t>(free_.size());
-  st->num_scale_pages = static_cast<int32_t>(scale_.size()) * unit_pages_;
-  st->num_window_pages = static_cast<int32_t>(window_.size()) * unit_pages_;
-  st->num_window_units = static_cast<int32_t>(window_.size());
+  st->num_scale_pages = static_cast<int32_t>(scale_.size());
+  st->num_window_pages = win_count_ * unit_pages_;
+  st->num_window_units = win_count_;
   st->num_special_pages = static_cast<int32_t>(special_.size());
   st->special_fill = fill_;
   st->num_units = n_;
   st->has_undo = has_undo_ ? 1 : 0;
   st->num_pages = num_pages_;
   if (st->free_pages) std::copy(free_.begin(), free_.end(), st->free_pages);
-  if (st->scale_pages) {
-    int32_t k = 0;
-    for (const auto& u : scale_)
-      for (int32_t p : u) st->scale_pages[k++] = p;
-  }
+  if (st->scale_pages) std::copy(scale_.begin(), scale_.end(), st->scale_pages);
   if (st->window_pages) {
     int32_t k = 0;
-    for (const auto& u : window_)
-      for (int32_t p : u) st->window_pages[k++] = p;
+    for (int32_t i = 0; i < win_count_; ++i) {
+      const int32_t* u = window_unit(i);
+      for (int32_t j = 0; j < unit_pages_; ++j) st->window_pages[k++] = u[j];
+    }
   }
   if (st->special_pages) std::copy(special_.begin(), special_.end(), st->special_pages);
 }

@@ -7,10 +7,12 @@
 // lengths, and the exact single-level rollback of section 3.  Units may be
 // chunks of frames ("vLLM-Omni RFC #2727: Reconstruction Engine", sections 1
 // and 2.3: the window keeps the most recent sliding_window_num chunks).
+//
+// All storage is sized at construction: plan, commit, rollback, reset and the
+// table and state queries allocate nothing and cannot throw.
 #pragma once
 
 #include <cstdint>
-#include <deque>
 #include <vector>
 
 #include "kvc.h"
@@ -19,7 +21,7 @@ namespace kvc {
 
 // Where one append puts its tokens; consumed by the scatter kernel.
 struct AppendPlan {
-  std::vector<int32_t> unit_pages;  // patch token i -> (unit_pages[i / P], i % P)
+  int32_t num_unit_pages = 0;       // patch token i -> (unit page i / P, slot i % P)
   int32_t special_page0 = -1;       // special token j < special_count0 -> (special_page0, special_slot0 + j)
   int32_t special_slot0 = 0;
   int32_t special_count0 = 0;
@@ -34,13 +36,20 @@ class PageCache {
   int32_t num_pages() const { return num_pages_; }
   int32_t unit_pages() const { return unit_pages_; }
 
-  // Plans and commits one append.  Returns KVC_OK or KVC_ERR_OUT_OF_PAGES
-  // (state unchanged).
-  int append(AppendPlan* plan);
+  // Plans the next append without changing any state: fills *plan and, when
+  // unit_pages is not null, the unit's num_unit_pages page ids.  Returns
+  // KVC_OK or KVC_ERR_OUT_OF_PAGES.
+  int plan(AppendPlan* plan, int32_t* unit_pages) const;
+  // Applies exactly the append plan() describes (call only after plan()
+  // returned KVC_OK on the unchanged cache).
+  void commit();
+  // plan() then commit().
+  int append();
   // Undoes the last append.  KVC_ERR_NO_UNDO when there is none.
   int rollback();
   void reset();
 
+  int32_t num_units() const { return n_; }
   int32_t visible_count() const;
   // Writes visible_count() entries.
   void visible_table(int32_t* ids, int32_t* lens) const;
@@ -50,30 +59,36 @@ class PageCache {
   static int validate(const kvc_config& cfg);
 
  private:
-  struct Undo {
-    std::vector<int32_t> unit;
-    std::vector<int32_t> evicted;
-    bool has_evicted = false;
-    int32_t new_special = -1;
-    int32_t prev_fill = 0;
-    bool to_scale = false;
-  };
-
   int32_t frames_per_special_page() const;
   int32_t full_special_len() const;
+  bool needs_special_page() const;
+  // Page list of window unit i (0 = oldest) inside the ring.
+  const int32_t* window_unit(int32_t i) const {
+    return win_.data() + static_cast<size_t>((win_head_ + i) % win_cap_) * unit_pages_;
+  }
+  int32_t* window_slot(int32_t i) {
+    return win_.data() + static_cast<size_t>((win_head_ + i) % win_cap_) * unit_pages_;
+  }
 
   kvc_config cfg_;
   int32_t num_pages_ = 0;
   int32_t unit_pages_ = 0;
   int32_t unit_tail_ = 0;
-  std::vector<int32_t> free_;  // stack; back() is the next page popped
-  std::vector<std::vector<int32_t>> scale_;
-  std::deque<std::vector<int32_t>> window_;
-  std::vector<int32_t> special_;
+  std::vector<int32_t> free_;     // stack; back() is the next page popped (capacity num_pages_)
+  std::vector<int32_t> scale_;    // scale units' pages in order, unit_pages_ per unit
+  std::vector<int32_t> win_;      // ring of win_cap_ window units, unit_pages_ pages each
+  int32_t win_cap_ = 0;
+  int32_t win_head_ = 0;          // ring slot of the oldest window unit
+  int32_t win_count_ = 0;
+  std::vector<int32_t> special_;  // special pages in the order they were opened
   int32_t fill_ = 0;
   int32_t n_ = 0;
+  // Undo record of the last append (single level).
   bool has_undo_ = false;
-  Undo undo_;
+  bool undo_to_scale_ = false;
+  bool undo_evicted_ = false;
+  int32_t undo_special_ = -1;     // special page the append opened, or -1
+  int32_t undo_prev_fill_ = 0;
 };
 
 }  // namespace kvc

@@ -1,0 +1,158 @@
+// Roofline probes: the chip's measured dense bf16 matrix-core rate and HBM
+// bandwidth, the denominators beside the published peaks (declared in
+// include/kvc_probe.h).  Each probe times a few launches of its kernel with
+// HIP events on the given stream and blocks until they are done.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "handle.hpp"
+#include "kvc.h"
+#include "kvc_probe.h"
+
+using kvc::fail;
+using kvc::guarded;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaIters = 4096;
+constexpr int kMfmaChains = 4;          // independent accumulators per wave
+constexpr int kMfmaThreads = 256;       // four waves, one per SIMD
+constexpr int kMfmaBlocks = 256 * 4;    // four workgroups per compute unit
+constexpr double kMfmaFlop = 32.0 * 32.0 * 16.0 * 2.0;  // one v_mfma_f32_32x32x16_bf16
+
+// Every wave issues kMfmaChains independent chains of 32x32x16 bf16 products
+// from registers; the operands never change, so the products are all the
+// kernel does.  One store per thread keeps the chains live.
+__global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(float* out, float seed) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(seed * static_cast<float>((threadIdx.x + i) & 7));
+    b[i] = static_cast<__bf16>(seed - static_cast<float>(i));
+  }
+  floatx16 c[kMfmaChains];
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j) c[j] = floatx16{};
+  for (int it = 0; it < kMfmaIters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c[j][i];
+  out[blockIdx.x * kMfmaThreads + threadIdx.x] = s;
+}
+
+constexpr int kCopyThreads = 256;
+
+// Streaming copy, 16 bytes per thread per step (grid-stride).
+__global__ __launch_bounds__(kCopyThreads) void copy_probe_kernel(const u32x4* __restrict__ src,
+                                                                  u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kCopyThreads;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kCopyThreads + threadIdx.x; i < n; i += stride)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+// Streaming read: every thread folds its 16-byte loads into one word and
+// stores it once (out holds one word per thread of the grid).
+__global__ __launch_bounds__(kCopyThreads) void read_probe_kernel(const u32x4* __restrict__ src, size_t n,
+                                                                  uint32_t* __restrict__ out) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kCopyThreads;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t t = static_cast<size_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+  for (size_t i = t; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  out[t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+constexpr int kStreamBlocks = 256 * 8;  // eight workgroups per compute unit
+constexpr int kReps = 5;
+
+// Times kReps launches of `launch` after one untimed launch; milliseconds per launch.
+template <class F>
+int time_launches(hipStream_t st, F&& launch, double* ms_per) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int status = KVC_OK;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    status = fail(KVC_ERR_DEVICE, "probe: hipEventCreate failed");
+  } else {
+    launch();
+    hipError_t e = hipEventRecord(e0, st);
+    for (int r = 0; r < kReps; ++r) launch();
+    if (e == hipSuccess) e = hipEventRecord(e1, st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e != hipSuccess)
+      status = fail(KVC_ERR_DEVICE, "probe: %s", hipGetErrorString(e));
+    else
+      *ms_per = static_cast<double>(ms) / kReps;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvc_probe_scratch_bytes(void) {
+  return std::max(static_cast<size_t>(kMfmaBlocks) * kMfmaThreads * sizeof(float),
+                  static_cast<size_t>(kStreamBlocks) * kCopyThreads * sizeof(uint32_t));
+}
+
+int kvc_probe_mfma_bf16(void* scratch, size_t scratch_bytes, kvc_stream_t stream, double* tflops) {
+  return guarded("kvc_probe_mfma_bf16", [&] {
+    if (!scratch || !tflops) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (scratch_bytes < kvc_probe_scratch_bytes())
+      return fail(KVC_ERR_BUFFER_TOO_SMALL, "scratch needs %zu bytes", kvc_probe_scratch_bytes());
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    double ms = 0.0;
+    const int s = time_launches(st, [&] {
+      hipLaunchKernelGGL(mfma_probe_kernel, dim3(kMfmaBlocks), dim3(kMfmaThreads), 0, st,
+                         static_cast<float*>(scratch), 0.5f);
+    }, &ms);
+    if (s) return s;
+    const double flop = kMfmaFlop * kMfmaChains * kMfmaIters * (kMfmaThreads / 64) * kMfmaBlocks;
+    *tflops = flop / (ms * 1e-3) / 1e12;
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+int kvc_probe_hbm(const void* src, void* dst, size_t bytes, void* scratch, size_t scratch_bytes,
+                  kvc_stream_t stream, double* read_gbs, double* copy_gbs) {
+  return guarded("kvc_probe_hbm", [&] {
+    if (!src || !dst || !scratch || !read_gbs || !copy_gbs) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (bytes < 16 || bytes % 16 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+      return fail(KVC_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16 and buffers 16-byte aligned");
+    if (scratch_bytes < kvc_probe_scratch_bytes())
+      return fail(KVC_ERR_BUFFER_TOO_SMALL, "scratch needs %zu bytes", kvc_probe_scratch_bytes());
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t n = bytes / 16;
+    double ms = 0.0;
+    int s = time_launches(st, [&] {
+      hipLaunchKernelGGL(read_probe_kernel, dim3(kStreamBlocks), dim3(kCopyThreads), 0, st,
+                         static_cast<const u32x4*>(src), n, static_cast<uint32_t*>(scratch));
+    }, &ms);
+    if (s) return s;
+    *read_gbs = static_cast<double>(bytes) / (ms * 1e-3) / 1e9;
+    s = time_launches(st, [&] {
+      hipLaunchKernelGGL(copy_probe_kernel, dim3(kStreamBlocks), dim3(kCopyThreads), 0, st,
+                         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    }, &ms);
+    if (s) return s;
+    *copy_gbs = 2.0 * static_cast<double>(bytes) / (ms * 1e-3) / 1e9;
+    return static_cast<int>(KVC_OK);
+  });
+}
+
+}  // extern "C"

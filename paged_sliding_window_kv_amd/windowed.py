@@ -2,90 +2,94 @@
 
 For very long streams the cache is restarted once per window: a window holds
 `window_slots` kept units (KV slots, i.e. stored keyframes, not raw frames),
-and adjacent windows share `overlap` units so that the next window starts
-aligned with the previous one.  Reading used (the page fixes neither the
-restart order nor where the shared units' K/V come from): when a window is
-full, the next append first resets the cache and re-appends the last
-`overlap` kept units of the finished window, oldest first.  Their K/V are the
-ones that were appended (in the model they would be recomputed in the new
-window).  The driver keeps those units in a fixed device ring, allocated
-once, so device memory stays constant however long the stream runs.
-
-Marshalling only: reset, append and rollback run in libkvc.so.
+and adjacent windows share `overlap` units.  The restart policy (reset, then
+re-append the last `overlap` kept units oldest first, with their appended
+K/V) runs in libkvc.so (kvc_windowed_*); this module allocates the two device
+rings that hold the shared units' K/V and marshals the calls.
 """
 from __future__ import annotations
 
+import ctypes as C
 from typing import Optional
 
-from .cache import KvCache
+from . import _lib as L
+from .cache import KvCache, current_stream_ptr, torch_dtype
 
 
 class WindowedStream:
     """Windowed appends over `cache`: append(k, v), then keep() or drop() the unit."""
 
     def __init__(self, cache: KvCache, window_slots: int = 128, overlap: int = 16):
-        if window_slots < 1 or not (0 <= overlap < window_slots):
-            raise ValueError("need window_slots >= 1 and 0 <= overlap < window_slots")
+        lib = L.lib()
         self.cache = cache
         self.window_slots = window_slots
         self.overlap = overlap
-        self.slots = 0          # kept units in the current window
-        self.windows = 0        # restarts so far
-        self._pending = None    # (k, v) of the unit appended last, until keep()/drop()
-        self._ring = None
-        self._ring_len = 0      # kept units in the ring (at most `overlap`)
-        self._ring_head = 0     # next ring slot to write
-        if cache.device is not None and overlap > 0:
+        self._ring = (None, None)
+        nb = C.c_size_t()
+        L.check(lib.kvc_windowed_ring_bytes(cache.handle, overlap, C.byref(nb)), "kvc_windowed_ring_bytes")
+        if nb.value:
             import torch
             shp = (overlap, cache.unit_tokens, cache.num_heads, cache.head_dim)
-            dt = cache.k_pool.dtype
-            self._ring = (torch.empty(shp, dtype=dt, device=cache.k_pool.device),
-                          torch.empty(shp, dtype=dt, device=cache.k_pool.device))
+            dt = torch_dtype(cache.dtype)
+            self._ring = tuple(torch.empty(shp, dtype=dt, device=cache.k_pool.device) for _ in range(2))
+            assert self._ring[0].numel() * self._ring[0].element_size() == nb.value
+        kr, vr = (None if r is None else r.data_ptr() for r in self._ring)
+        h = C.c_void_p()
+        L.check(lib.kvc_windowed_create(cache.handle, window_slots, overlap, kr, vr, C.byref(h)),
+                "kvc_windowed_create")
+        self._h = h
+        self._pending = None  # keeps the appended tensors alive until keep()/drop()
 
-    def _restart(self, stream: Optional[int]) -> None:
-        self.cache.reset()
-        n = self._ring_len
-        for j in range(n):
-            slot = (self._ring_head - n + j) % self.overlap
-            if self._ring is None:
-                self.cache.append(stream=stream)
-            else:
-                self.cache.append(self._ring[0][slot], self._ring[1][slot], stream=stream)
-        self.slots = n
-        self.windows += 1
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            L.lib().kvc_windowed_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _state(self) -> L.KvcWindowedState:
+        st = L.KvcWindowedState()
+        L.check(L.lib().kvc_windowed_get_state(self._h, C.byref(st)), "kvc_windowed_get_state")
+        return st
+
+    @property
+    def slots(self) -> int:
+        return self._state().slots
+
+    @property
+    def windows(self) -> int:
+        return self._state().windows
 
     def append(self, k=None, v=None, stream: Optional[int] = None) -> bool:
         """Append one unit; returns True when this append started a new window."""
-        if self._pending is not None:
-            raise RuntimeError("keep() or drop() the previous unit first")
-        restarted = False
-        if self.slots >= self.window_slots:
-            self._restart(stream)
-            restarted = True
-        if self.cache.device is None:
-            self.cache.append()
+        c = self.cache
+        if c.device is None:
+            if k is not None or v is not None:
+                raise ValueError("host-only cache takes no K/V")
+            kp = vp = s = None
         else:
-            self.cache.append(k, v, stream=stream)
+            c._check_unit(k, "k")
+            c._check_unit(v, "v")
+            kp, vp = k.data_ptr(), v.data_ptr()
+            s = current_stream_ptr(k.device) if stream is None else stream
+        r = C.c_int32()
+        L.check(L.lib().kvc_windowed_append(self._h, kp, vp, s, C.byref(r)), "kvc_windowed_append")
         self._pending = (k, v)
-        return restarted
+        return bool(r.value)
 
-    def keep(self) -> None:
+    def keep(self, stream: Optional[int] = None) -> None:
         """The last unit is a keyframe: it stays, takes one slot and enters the overlap ring."""
-        if self._pending is None:
-            raise RuntimeError("nothing appended")
-        k, v = self._pending
+        s = None
+        if self.cache.device is not None:
+            s = current_stream_ptr(self.cache.k_pool.device) if stream is None else stream
+        L.check(L.lib().kvc_windowed_keep(self._h, s), "kvc_windowed_keep")
         self._pending = None
-        self.slots += 1
-        if self.overlap > 0:
-            if self._ring is not None:
-                self._ring[0][self._ring_head].copy_(k)
-                self._ring[1][self._ring_head].copy_(v)
-            self._ring_head = (self._ring_head + 1) % self.overlap
-            self._ring_len = min(self._ring_len + 1, self.overlap)
 
     def drop(self) -> None:
         """The last unit is not kept (keyframe skip): roll it back."""
-        if self._pending is None:
-            raise RuntimeError("nothing appended")
+        L.check(L.lib().kvc_windowed_drop(self._h), "kvc_windowed_drop")
         self._pending = None
-        self.cache.rollback()
