@@ -6,6 +6,12 @@ adjacent windows share `overlap` units.  Reading: when a window is full, the
 next append first resets the cache and re-appends the last `overlap` kept
 units of the finished window (oldest first, the K/V that were appended);
 non-kept units (keyframe skips) take no slot and are rolled back.
+
+Pinned by tests/test_oracle_windowed.py: a 15-frame trace derived by hand
+from these readings (tests/golden/windowed_trace.json: restart frames, tables
+and the frame every visible token comes from), which planted mistakes (a
+restart one slot late or early, the shared units re-appended newest first,
+dropped units entering the shared ring or taking slots) each fail.
 """
 from __future__ import annotations
 
