@@ -27,8 +27,8 @@ fourth frame and rolls the others back).
 
 Every workload reports `roofline` for its dominant kernel (algorithmic FLOPs
 or bytes per launch over the kernel's own duration, taken with HIP events on
-the launch stream: the library records an event right after the attention
-kernel and before the merge of split partials) and `cpu_baseline` (the
+the launch stream: the library records events right before and right after
+the attention kernel, before the merge of split partials) and `cpu_baseline` (the
 oracle timed on the host on a bounded slice of the same workload).
 """
 from __future__ import annotations
@@ -133,17 +133,19 @@ def cpu_baseline(value: float, unit: str, sample: str, sec: float, extra: dict |
 class CallClock:
     """HIP events around attention calls on the launch stream.
 
-    For call i: `before(i)` records a start event and hands the library a
-    kernel-done event, which it records right after the attention kernel (and
-    before the merge of split partials); `after(i)` records an end event.
-    start -> kernel-done is the attention kernel alone, start -> end the call.
+    For call i: `before(i)` records a call-start event and hands the library
+    a kernel-start and a kernel-done event, which it records right before and
+    right after the attention kernel (after its host-side table work, before
+    the merge of split partials); `after(i)` records a call-end event.
+    kernel-start -> kernel-done is the attention kernel alone, call-start ->
+    call-end the whole call.
     """
 
     def __init__(self, n: int):
         import torch
         from paged_sliding_window_kv_amd import lib
         self.torch, self.lib = torch, lib()
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
         for trio in self.ev:  # torch creates the HIP events at their first record
             for e in trio:
                 e.record()
@@ -154,18 +156,19 @@ class CallClock:
 
     def before(self, i: int) -> None:
         self.ev[i][0].record()
-        _ok(self.lib.kvc_set_kernel_done_event(C.c_void_p(self.ev[i][1].cuda_event)), "kvc_set_kernel_done_event")
+        _ok(self.lib.kvc_set_kernel_events(C.c_void_p(self.ev[i][1].cuda_event), C.c_void_p(self.ev[i][2].cuda_event)),
+            "kvc_set_kernel_events")
 
     def after(self, i: int) -> None:
-        self.ev[i][2].record()
-        _ok(self.lib.kvc_set_kernel_done_event(None), "kvc_set_kernel_done_event")
+        self.ev[i][3].record()
+        _ok(self.lib.kvc_set_kernel_events(None, None), "kvc_set_kernel_events")
 
     def collect(self, n: int) -> None:
         """Adds calls 0..n-1 (after a synchronize) to the totals."""
         self.torch.cuda.synchronize()
         for i in range(n):
-            s, k, e = self.ev[i]
-            self.kernel_s += s.elapsed_time(k) * 1e-3
+            s, k0, k1, e = self.ev[i]
+            self.kernel_s += k0.elapsed_time(k1) * 1e-3
             self.call_s += s.elapsed_time(e) * 1e-3
         self.calls += n
 
@@ -189,7 +192,8 @@ def run_probes() -> dict:
     del src, dst, scratch
     torch.cuda.empty_cache()
     out = {"mfma_bf16_tflops": tf.value, "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
-           "mfma_probe": "1,024 workgroups x 4 waves x 4 chains of v_mfma_f32_32x32x16_bf16 from registers",
+           "mfma_probe": "one 16-wave workgroup per compute unit, 4 chains of v_mfma_f32_32x32x16_bf16 per wave, "
+                         "from registers",
            "hbm_probe": "2 GiB streaming read (16-byte loads) and 2 GiB copy (read + write bytes)"}
     log(f"[bench] probes: bf16 matrix cores {tf.value:.0f} TFLOP/s, HBM read {rd.value:.0f} GB/s, "
         f"copy {cp.value:.0f} GB/s")
@@ -1023,9 +1027,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-extras", action="store_true", help="chunked: skip the LingBot stream and the probes")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB device copy and exit (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="chunked/global oracle slice: query rows of one layer (all heads)")
-    ap.add_argument("--cpu-sample", type=int, default=4, help="stream oracle sample: last frames of one layer")
+    ap.add_argument("--cpu-sample", type=int, default=24, help="stream oracle sample: last frames of one layer")
     args = ap.parse_args(argv)
     if args.steps is None:
         args.steps = DEFAULT_STEPS[args.workload]

@@ -427,12 +427,12 @@ const char* kvc_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */
 int kvc_version(void);
 
-/* Measurement hook for timing the attention kernel apart from the merge of
- * split partials: while `event` (a hipEvent_t) is not NULL, every attention
- * call made on the calling thread records it on its launch stream right after
- * the attention kernel and before the merge.  An event recorded before the
- * call and this one then bracket the kernel alone.  NULL turns it off. */
-int kvc_set_kernel_done_event(void* event);
+/* Measurement hook for timing the attention kernel apart from the host-side
+ * table work and the merge of split partials: while set, every attention call
+ * made on the calling thread records `start` (a hipEvent_t, or NULL) on its
+ * launch stream right before the attention kernel and `done` (or NULL) right
+ * after it, before the merge.  Both NULL turns it off. */
+int kvc_set_kernel_events(void* start, void* done);
 
 #ifdef __cplusplus
 }

@@ -27,9 +27,9 @@ extern "C" {
 /* Bytes of the device scratch buffer each probe writes its results into. */
 size_t kvc_probe_scratch_bytes(void);
 
-/* Dense bf16 matrix-core rate: 1,024 workgroups of four waves, each wave
- * issuing four independent chains of v_mfma_f32_32x32x16_bf16 from registers
- * (32*32*16*2 FLOP each).  *tflops receives the rate in TFLOP/s.
+/* Dense bf16 matrix-core rate: one workgroup of sixteen waves (four per SIMD)
+ * per compute unit, each wave issuing four independent chains of
+ * v_mfma_f32_32x32x16_bf16 from registers (32*32*16*2 FLOP each).  *tflops receives the rate in TFLOP/s.
  * scratch: device buffer of kvc_probe_scratch_bytes. */
 int kvc_probe_mfma_bf16(void* scratch, size_t scratch_bytes, kvc_stream_t stream, double* tflops);
 

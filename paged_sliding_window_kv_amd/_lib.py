@@ -36,7 +36,7 @@ EXPORTED = (
     "kvc_build_subset_table", "kvc_attend_subset",
     "kvc_windowed_ring_bytes", "kvc_windowed_create", "kvc_windowed_destroy", "kvc_windowed_append",
     "kvc_windowed_keep", "kvc_windowed_drop", "kvc_windowed_get_state",
-    "kvc_strerror", "kvc_last_error", "kvc_version", "kvc_set_kernel_done_event",
+    "kvc_strerror", "kvc_last_error", "kvc_version", "kvc_set_kernel_events",
     # include/kvc_probe.h
     "kvc_probe_scratch_bytes", "kvc_probe_mfma_bf16", "kvc_probe_hbm",
 )
@@ -148,7 +148,7 @@ def _declare(lib):
         "kvc_windowed_keep": (C.c_int, [vp, vp]),
         "kvc_windowed_drop": (C.c_int, [vp]),
         "kvc_windowed_get_state": (C.c_int, [vp, C.POINTER(KvcWindowedState)]),
-        "kvc_set_kernel_done_event": (C.c_int, [vp]),
+        "kvc_set_kernel_events": (C.c_int, [vp, vp]),
         "kvc_probe_scratch_bytes": (C.c_size_t, []),
         "kvc_probe_mfma_bf16": (C.c_int, [vp, C.c_size_t, vp, C.POINTER(C.c_double)]),
         "kvc_probe_hbm": (C.c_int, [vp, vp, C.c_size_t, vp, C.c_size_t, vp, C.POINTER(C.c_double),

@@ -23,8 +23,10 @@ namespace kvc {
 
 namespace {
 thread_local char g_last_error[512] = "";
-// Measurement hook (kvc_set_kernel_done_event): recorded on the launch stream
-// right after each attention kernel, before the merge of split partials.
+// Measurement hook (kvc_set_kernel_events): recorded on the launch stream
+// right before and right after each attention kernel (before the merge of
+// split partials).
+thread_local hipEvent_t g_kernel_start = nullptr;
 thread_local hipEvent_t g_kernel_done = nullptr;
 }  // namespace
 
@@ -268,6 +270,10 @@ int setup_attn(const paged_attn_args& a, kvc::AttnParams& p, int* splits_out) {
 template <class Src>
 int launch_attn(const paged_attn_args& a, const Src& src, int splits, hipStream_t st) {
   const kvc::AttnParams& p = kvc::attn_base(src);
+  if (kvc::g_kernel_start) {
+    const hipError_t e = hipEventRecord(kvc::g_kernel_start, st);
+    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "recording the kernel-start event: %s", hipGetErrorString(e));
+  }
   hipError_t e = a.dtype == KVC_DTYPE_BF16        ? kvc::launch_attn_bf16(src, choose_waves(a), st)
                  : a.dtype == KVC_DTYPE_FP8_E4M3 ? kvc::launch_attn_fp8kv(src, choose_waves(a), st)
                                                  : kvc::launch_attn_f32(src, st);
@@ -793,8 +799,9 @@ int paged_attn_merge(int32_t dtype, int32_t num_parts, int32_t rows, int32_t num
   });
 }
 
-int kvc_set_kernel_done_event(void* event) {
-  kvc::g_kernel_done = static_cast<hipEvent_t>(event);
+int kvc_set_kernel_events(void* start, void* done) {
+  kvc::g_kernel_start = static_cast<hipEvent_t>(start);
+  kvc::g_kernel_done = static_cast<hipEvent_t>(done);
   return KVC_OK;
 }
 

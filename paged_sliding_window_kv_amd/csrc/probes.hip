@@ -22,14 +22,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaIters = 4096;
 constexpr int kMfmaChains = 4;          // independent accumulators per wave
-constexpr int kMfmaThreads = 256;       // four waves, one per SIMD
-constexpr int kMfmaBlocks = 256 * 4;    // four workgroups per compute unit
+constexpr int kMfmaThreads = 1024;      // sixteen waves, four per SIMD
+constexpr int kMfmaMaxBlocks = 1024;    // scratch sizing: at most this many compute units
+constexpr int kMfmaPadFloats = 96 * 1024 / 4;  // 96 KiB of LDS: one workgroup per compute unit
 constexpr double kMfmaFlop = 32.0 * 32.0 * 16.0 * 2.0;  // one v_mfma_f32_32x32x16_bf16
 
-// Every wave issues kMfmaChains independent chains of 32x32x16 bf16 products
-// from registers; the operands never change, so the products are all the
-// kernel does.  One store per thread keeps the chains live.
+// One workgroup per compute unit (its LDS leaves no room for a second), every
+// wave issuing kMfmaChains independent chains of 32x32x16 bf16 products from
+// registers; the operands never change, so the products are all the kernel
+// does.  One store per thread keeps the chains live.
 __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(float* out, float seed) {
+  __shared__ float pad[kMfmaPadFloats];
+  pad[threadIdx.x] = seed;
   bf16x8 a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -43,7 +47,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(float* out, fl
 #pragma unroll
     for (int j = 0; j < kMfmaChains; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
   }
-  float s = 0.f;
+  __syncthreads();
+  float s = pad[(threadIdx.x + 1) % kMfmaThreads];
 #pragma unroll
   for (int j = 0; j < kMfmaChains; ++j)
 #pragma unroll
@@ -106,7 +111,7 @@ int time_launches(hipStream_t st, F&& launch, double* ms_per) {
 extern "C" {
 
 size_t kvc_probe_scratch_bytes(void) {
-  return std::max(static_cast<size_t>(kMfmaBlocks) * kMfmaThreads * sizeof(float),
+  return std::max(static_cast<size_t>(kMfmaMaxBlocks) * kMfmaThreads * sizeof(float),
                   static_cast<size_t>(kStreamBlocks) * kCopyThreads * sizeof(uint32_t));
 }
 
@@ -116,13 +121,18 @@ int kvc_probe_mfma_bf16(void* scratch, size_t scratch_bytes, kvc_stream_t stream
     if (scratch_bytes < kvc_probe_scratch_bytes())
       return fail(KVC_ERR_BUFFER_TOO_SMALL, "scratch needs %zu bytes", kvc_probe_scratch_bytes());
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return fail(KVC_ERR_DEVICE, "probe: cannot read the compute-unit count");
+    const int blocks = std::min(cus, kMfmaMaxBlocks);
     double ms = 0.0;
     const int s = time_launches(st, [&] {
-      hipLaunchKernelGGL(mfma_probe_kernel, dim3(kMfmaBlocks), dim3(kMfmaThreads), 0, st,
-                         static_cast<float*>(scratch), 0.5f);
+      hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(kMfmaThreads), 0, st, static_cast<float*>(scratch),
+                         0.5f);
     }, &ms);
     if (s) return s;
-    const double flop = kMfmaFlop * kMfmaChains * kMfmaIters * (kMfmaThreads / 64) * kMfmaBlocks;
+    const double flop = kMfmaFlop * kMfmaChains * kMfmaIters * (kMfmaThreads / 64) * blocks;
     *tflops = flop / (ms * 1e-3) / 1e12;
     return static_cast<int>(KVC_OK);
   });
