@@ -359,6 +359,30 @@ int kvc_attend_batch(const kvc_t* const* caches, int32_t num_caches, const void*
 int kvc_attend_batch_workspace_size(const kvc_t* const* caches, int32_t num_caches, const int32_t* qo_indptr,
                                     size_t* bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): kvc_attend
+ * without a workspace argument.  The split partials live in a device array
+ * inside the library, KVC_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU it runs
+ * on, held until the process ends; its address is looked up once per device
+ * (on the first call made with that device current).  Nothing is allocated:
+ * no device memory, no pinned staging, no host heap.
+ *   - Tables must travel in the launch arguments: more than 640 visible
+ *     entries gives KVC_ERR_UNSUPPORTED (use kvc_attend).
+ *   - The split count is kvc_attend's whenever its partials fit the array
+ *     (then results are identical to kvc_attend's); otherwise the largest
+ *     split count whose partials fit is used (one split needs none), so
+ *     results differ from kvc_attend's only by the rounding of the merge.
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap on
+ *     one GPU (concurrent streams, or threads) race and give wrong results.
+ *     Calls enqueued on one stream are ordered and safe.  The array needs no
+ *     clearing: each call writes every partial it reads.
+ *   - The current device must be the device of `stream`
+ *     (KVC_ERR_INVALID_ARGUMENT otherwise).
+ * Other arguments and errors as kvc_attend. */
+#define KVC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int kvc_attend_noalloc(const kvc_t* cache, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+                       kvc_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Windowed inference ("LingBot-Map Paged KV Cache", section 4)              */
 /* ------------------------------------------------------------------------ */

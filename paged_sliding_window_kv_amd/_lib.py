@@ -33,7 +33,7 @@ EXPORTED = (
     "kvc_rollback_last_frame", "kvc_reset", "kvc_build_visible_table", "kvc_get_state",
     "paged_attn_workspace_size", "paged_attn_num_splits", "paged_attn_fwd", "paged_attn_merge",
     "kvc_attend", "kvc_attend_workspace_size", "kvc_attend_batch", "kvc_attend_batch_workspace_size",
-    "kvc_build_subset_table", "kvc_attend_subset",
+    "kvc_build_subset_table", "kvc_attend_subset", "kvc_attend_noalloc",
     "kvc_windowed_ring_bytes", "kvc_windowed_create", "kvc_windowed_destroy", "kvc_windowed_append",
     "kvc_windowed_keep", "kvc_windowed_drop", "kvc_windowed_get_state",
     "kvc_strerror", "kvc_last_error", "kvc_version", "kvc_set_kernel_events",
@@ -41,6 +41,7 @@ EXPORTED = (
     "kvc_probe_scratch_bytes", "kvc_probe_mfma_bf16", "kvc_probe_hbm",
 )
 MAX_INLINE_PAGES = 640
+NOALLOC_SCRATCH_BYTES = 32 << 20
 MAX_BATCH_CACHES = 16
 
 
@@ -141,6 +142,7 @@ def _declare(lib):
                                         C.c_size_t, vp]),
         "kvc_attend_batch": (C.c_int, [C.POINTER(vp), i32, vp, i32p, C.c_float, vp, vp, vp, C.c_size_t, vp]),
         "kvc_attend_batch_workspace_size": (C.c_int, [C.POINTER(vp), i32, i32p, C.POINTER(C.c_size_t)]),
+        "kvc_attend_noalloc": (C.c_int, [vp, vp, i32, C.c_float, vp, vp, vp]),
         "kvc_windowed_ring_bytes": (C.c_int, [vp, i32, C.POINTER(C.c_size_t)]),
         "kvc_windowed_create": (C.c_int, [vp, i32, i32, vp, vp, C.POINTER(vp)]),
         "kvc_windowed_destroy": (C.c_int, [vp]),

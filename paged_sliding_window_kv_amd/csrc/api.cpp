@@ -324,6 +324,23 @@ bool inline_table_ok(const kvc_t* c, int32_t n) {
 // entries: ids, lens, then the query and entry index pairs of one sequence.
 size_t table_region_bytes(int32_t n) { return (static_cast<size_t>(2 * n + 4) * sizeof(int32_t) + 255) & ~size_t(255); }
 
+// Launch over a table that travels in the launch arguments (n <=
+// kMaxInlinePages entries; a.q, a.o, a.lse, a.workspace set).
+int launch_inline(paged_attn_args& a, const int32_t* ids, const int32_t* lens, int32_t n, hipStream_t st) {
+  if (int s = check_attn_args(&a)) return s;
+  static thread_local kvc::AttnParamsInline pi;
+  int splits = 1;
+  if (int s = setup_attn(a, pi.base, &splits)) return s;
+  pi.num_entries = n;
+  pi.qo[0] = 0;
+  pi.qo[1] = a.total_q;
+  pi.kv[0] = 0;
+  pi.kv[1] = n;
+  for (int32_t i = 0; i < n; ++i)
+    pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
+  return launch_attn(a, pi, splits, st);
+}
+
 // Attention of one cache's queries over an explicit table (ids, lens; n
 // entries of this cache's pool).  Tables of up to 640 entries travel in the
 // launch arguments; longer ones are staged in pinned host memory and copied
@@ -343,18 +360,7 @@ int attend_table(const kvc_t* c, const int32_t* ids, const int32_t* lens, int32_
   if (inline_table_ok(c, n)) {
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    if (int s = check_attn_args(&a)) return s;
-    static thread_local kvc::AttnParamsInline pi;
-    int splits = 1;
-    if (int s = setup_attn(a, pi.base, &splits)) return s;
-    pi.num_entries = n;
-    pi.qo[0] = 0;
-    pi.qo[1] = num_q;
-    pi.kv[0] = 0;
-    pi.kv[1] = n;
-    for (int32_t i = 0; i < n; ++i)
-      pi.entries[i] = static_cast<uint32_t>(ids[i]) | (static_cast<uint32_t>(lens[i]) << kvc::kInlinePidBits);
-    return launch_attn(a, pi, splits, st);
+    return launch_inline(a, ids, lens, n, st);
   }
   // device table at the start of the workspace, split partials after it
   const size_t tb = table_region_bytes(n);
@@ -469,6 +475,39 @@ int batch_args(const kvc_t* const* caches, int32_t n, const int32_t* qo, float s
 }
 
 }  // namespace
+
+namespace kvc {
+
+int attend_fixed_workspace(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, kvc_stream_t stream) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (!c->k_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache has no device pools");
+  if (num_q < 0 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "bad num_q or sm_scale");
+  if (num_q == 0) return KVC_OK;
+  if (!q || !o) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL q or o");
+  const int32_t n = c->pc.visible_count();
+  if (!inline_table_ok(c, n))
+    return fail(KVC_ERR_UNSUPPORTED,
+                "the visible table has %d entries; without allocation at most %d travel in the launch arguments "
+                "(longer tables need staging memory: use kvc_attend)", n, kvc::kMaxInlinePages);
+  int32_t ids[kvc::kMaxInlinePages], lens[kvc::kMaxInlinePages];
+  c->pc.visible_table(ids, lens);
+  paged_attn_args a = cache_attn_args(c, num_q, n, sm_scale);
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (int s = check_attn_args(&a)) return s;
+  // The split count kvc_attend would take, or the largest whose partials fit.
+  int splits = choose_splits(a);
+  while (splits > 1 && workspace_for(a, splits) > workspace_bytes) --splits;
+  a.num_splits = splits;
+  return launch_inline(a, ids, lens, n, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace kvc
 
 extern "C" {
 

@@ -60,6 +60,12 @@ int guarded(const char* where, F&& body) noexcept {
   }
 }
 
+// kvc_attend over a caller-given workspace of workspace_bytes, allocating
+// nothing: only tables that travel in the launch arguments (up to 640
+// entries), and the split count is lowered until the partials fit.
+int attend_fixed_workspace(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, kvc_stream_t stream);
+
 // Element bytes of appended K/V activations (FP8 caches take bf16).
 inline size_t activation_bytes(int dtype) { return dtype == KVC_DTYPE_F32 ? 4 : 2; }
 
