@@ -1576,6 +1576,104 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) pb[t] = to_bf16x8(t < 2 ? s0 : s1, 8 * (t & 1));
   };
+  // Probabilities of elements b..b+3 of s against -nm's maximum, in place;
+  // returns their sum.
+  auto probs4 = [&](floatx16& s, int b, float nm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[b + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b + r], sl2, nm));
+    return (s[b] + s[b + 1]) + (s[b + 2] + s[b + 3]);
+  };
+  // Rare path of the interleaved tile: as softmax() when the lane sum is out of bounds.
+  auto rescale = [&](floatx16& s0, floatx16& s1, float& m, float& l, floatx16& o0, floatx16& o1,
+                     const uint16_t* lk, const bf16x8 (&qv)[4], int nk) {
+    bf16x8 kf[8];
+    kfrags(lk, kf);
+    scores(kf, qv, s0, s1);
+    if (nk < KT) mask(s0, s1, nk);
+    const float m_new = fmaxf(m, pair_max(tile_max(s0, s1)) * sl2);
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o0[r] *= alpha;
+      o1[r] *= alpha;
+    }
+    const float nm = -m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, nm));
+      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, nm));
+    }
+    return tile_sum(s0, s1);
+  };
+  // One tile with each block's softmax issued beside the other block's
+  // products: a wave's VALU work runs beside matrix products only when the
+  // same wave issues them interleaved, so the tile is laid out as fenced
+  // groups of one product plus a four-element slice of a softmax:
+  //   block A's 8 score products; 8 x (one of block B's score products, a
+  //   slice of block A's softmax); rare path A; block A's probabilities to
+  //   bf16 and the V fragments; 8 x (one of block A's P V products, a slice
+  //   of block B's softmax); rare path B; block B's 8 P V products.
+  auto tile_interleaved = [&](const uint16_t* lk, int nk, bool first) {
+    bf16x8 kf[8];
+    kfrags(lk, kf);
+    floatx16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qa[st], sa0, 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[4 + st], qa[st], sa1, 0, 0, 0);
+    if (nk < KT) mask(sa0, sa1, nk);
+    if (first) ma = pair_max(tile_max(sa0, sa1)) * sl2;  // every tile holds a valid key
+    __builtin_amdgcn_sched_barrier(0);
+    float ps[8];
+    const float nma = -ma;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < 4)
+        sb0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[i], sb0, 0, 0, 0);
+      else
+        sb1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[i - 4], sb1, 0, 0, 0);
+      ps[i] = probs4(i < 4 ? sa0 : sa1, 4 * (i & 3), nma);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float lta = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    if (__any(!(lta <= kSumBound))) lta = rescale(sa0, sa1, ma, la, oa0, oa1, lk, qa, nk);
+    la += lta;
+    if (nk < KT) mask(sb0, sb1, nk);
+    if (first) mb = pair_max(tile_max(sb0, sb1)) * sl2;
+    bf16x8 pa[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pa[t] = to_bf16x8(t < 2 ? sa0 : sa1, 8 * (t & 1));
+    const uint16_t* lv = lk + TILE_ELEMS;
+    bf16x8 vf[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      vf[t] = lds_frag(lv, lr, 2 * t + lh);
+      vf[4 + t] = lds_frag(lv, 32 + lr, 2 * t + lh);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float nmb = -mb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < 4)
+        oa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pa[i], oa0, 0, 0, 0);
+      else
+        oa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pa[i - 4], oa1, 0, 0, 0);
+      ps[i] = probs4(i < 4 ? sb0 : sb1, 4 * (i & 3), nmb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float ltb = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    if (__any(!(ltb <= kSumBound))) ltb = rescale(sb0, sb1, mb, lb, ob0, ob1, lk, qb, nk);
+    lb += ltb;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pb[t] = to_bf16x8(t < 2 ? sb0 : sb1, 8 * (t & 1));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ob0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pb[t], ob0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ob1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + t], pb[t], ob1, 0, 0, 0);
+  };
 
   // ---- the key loop: tile j lives in stage j % STAGES ------------------------
   Cursor lc, cc;
@@ -1624,35 +1722,7 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
       __builtin_amdgcn_s_barrier();
     }
-    if (active) {
-      bf16x8 kf[8];
-      kfrags(lk, kf);
-      floatx16 sa0, sa1, sb0, sb1;
-      scores(kf, qa, sa0, sa1);
-      scores(kf, qb, sb0, sb1);
-      if (nk < KT) {
-        mask(sa0, sa1, nk);
-        mask(sb0, sb1, nk);
-      }
-      bf16x8 pa[4], pbb[4];
-      softmax(sa0, sa1, ma, la, oa0, oa1, lk, qa, nk, j == 0, pa);
-      const uint16_t* lv = lk + TILE_ELEMS;
-      bf16x8 vf[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        vf[t] = lds_frag(lv, lr, 2 * t + lh);
-        vf[4 + t] = lds_frag(lv, 32 + lr, 2 * t + lh);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) oa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pa[t], oa0, 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) oa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + t], pa[t], oa1, 0, 0, 0);
-      softmax(sb0, sb1, mb, lb, ob0, ob1, lk, qb, nk, j == 0, pbb);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) ob0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pbb[t], ob0, 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) ob1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 + t], pbb[t], ob1, 0, 0, 0);
-    }
+    if (active) tile_interleaved(lk, nk, j == 0);
     cursor_next(src, ee, cc);
     ++j;
   }
