@@ -137,8 +137,11 @@ class CallClock:
     a kernel-start and a kernel-done event, which it records right before and
     right after the attention kernel (after its host-side table work, before
     the merge of split partials); `after(i)` records a call-end event.
-    kernel-start -> kernel-done is the attention kernel alone, call-start ->
-    call-end the whole call.
+    kernel-start -> kernel-done is the attention kernel alone; kernel-start ->
+    call-end is the kernel plus the merge of its split partials.  The call's
+    host-side table work before the launch is left out: while the host is
+    slower than the GPU (a 40 us kernel against four event records and a
+    ctypes call per layer), it would time the host, not the device.
     """
 
     def __init__(self, n: int):
@@ -167,9 +170,9 @@ class CallClock:
         """Adds calls 0..n-1 (after a synchronize) to the totals."""
         self.torch.cuda.synchronize()
         for i in range(n):
-            s, k0, k1, e = self.ev[i]
+            _, k0, k1, e = self.ev[i]
             self.kernel_s += k0.elapsed_time(k1) * 1e-3
-            self.call_s += s.elapsed_time(e) * 1e-3
+            self.call_s += k0.elapsed_time(e) * 1e-3
         self.calls += n
 
 
@@ -480,6 +483,8 @@ def run_stream(args, timed: int | None = None, cpu_sample: int | None = None) ->
     mem0 = torch.cuda.memory_allocated(b.dev)  # pools, inputs, outputs, workspace
     for t in range(frames - timed):
         b.step(t)
+        if (t + 1) % 250 == 0:
+            log(f"[bench] stream: untimed frame {t + 1}")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(frames - timed, frames):
@@ -500,6 +505,8 @@ def run_stream(args, timed: int | None = None, cpu_sample: int | None = None) ->
     byt = flo = 0.0
     for t in range(frames):
         b.step(t, clock)
+        if (t + 1) % 250 == 0:
+            log(f"[bench] stream: event replay frame {t + 1}")
         lk = stream_lk(t)
         byt += layers * attn_bytes(b.tokens, lk, heads, kv_elem=b.kv_elem)
         flo += layers * attn_flops(b.tokens, lk, heads)

@@ -193,8 +193,9 @@ def test_split_choice_and_workspace():
     # rounds of the chip unsplit; 5 splits give 7 rounds, the last 88% full
     a.num_splits, a.total_q, a.max_qo_len, a.max_kv_pages = 0, 10992, 10992, 172
     assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 5
-    # 100 frames x 1374 queries over 537 pages: 4,304 tiles nearly fill 17 rounds, no split
-    a.total_q, a.max_qo_len, a.max_kv_pages = 137400, 137400, 537
+    # 100 frames x 1374 queries over 600 pages (100 one-frame units of 6 pages):
+    # 4,304 tiles nearly fill 17 rounds, no split
+    a.total_q, a.max_qo_len, a.max_kv_pages = 137400, 137400, 600
     assert lib.paged_attn_num_splits(C.byref(a), C.byref(ns)) == 0 and ns.value == 1
 
 
