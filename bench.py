@@ -177,7 +177,9 @@ class CallClock:
 
 
 def run_probes() -> dict:
-    """Measured denominators: dense bf16 matrix-core rate and HBM read/copy bandwidth (include/kvc_probe.h)."""
+    """Measured denominators (include/kvc_probe.h): dense bf16 matrix-core rate, the 512-row attention kernel's
+    per-tile instruction mix on its own (products and softmax from registers and LDS, no global memory or table
+    walk), and HBM read/copy bandwidth."""
     import torch
     from paged_sliding_window_kv_amd import lib
     lb = lib()
@@ -186,6 +188,8 @@ def run_probes() -> dict:
     scratch = torch.empty(lb.kvc_probe_scratch_bytes(), dtype=torch.uint8, device=dev)
     tf = C.c_double()
     _ok(lb.kvc_probe_mfma_bf16(scratch.data_ptr(), scratch.numel(), sp, C.byref(tf)), "kvc_probe_mfma_bf16")
+    mix = C.c_double()
+    _ok(lb.kvc_probe_tile_mix(scratch.data_ptr(), scratch.numel(), sp, C.byref(mix)), "kvc_probe_tile_mix")
     nb = 2 << 30
     src = torch.ones(nb, dtype=torch.uint8, device=dev)
     dst = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -194,12 +198,16 @@ def run_probes() -> dict:
                          C.byref(cp)), "kvc_probe_hbm")
     del src, dst, scratch
     torch.cuda.empty_cache()
-    out = {"mfma_bf16_tflops": tf.value, "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
+    out = {"mfma_bf16_tflops": tf.value, "tile_mix_tflops": mix.value, "hbm_read_gbs": rd.value,
+           "hbm_copy_gbs": cp.value,
            "mfma_probe": "one 16-wave workgroup per compute unit, 4 chains of v_mfma_f32_32x32x16_bf16 per wave, "
                          "from registers",
+           "tile_mix_probe": "attn_wide_kernel's per-tile work without global memory, table walk, masks or rare-path "
+                             "checks: 8 waves per compute unit, per wave and 64-key tile one barrier, 16 LDS fragment "
+                             "reads, 32 products and two 32-row blocks' softmax in fenced groups",
            "hbm_probe": "2 GiB streaming read (16-byte loads) and 2 GiB copy (read + write bytes)"}
-    log(f"[bench] probes: bf16 matrix cores {tf.value:.0f} TFLOP/s, HBM read {rd.value:.0f} GB/s, "
-        f"copy {cp.value:.0f} GB/s")
+    log(f"[bench] probes: bf16 matrix cores {tf.value:.0f} TFLOP/s, attention tile mix {mix.value:.0f} TFLOP/s, "
+        f"HBM read {rd.value:.0f} GB/s, copy {cp.value:.0f} GB/s")
     return out
 
 
@@ -969,13 +977,41 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def code_text(text: str, line_comment: str) -> str:
+    """The text without comments, trailing blanks or empty lines: what the compiler sees of it (string literals
+    are kept whole)."""
+    out = []
+    for line in text.splitlines():
+        quote = None
+        cut = len(line)
+        i = 0
+        while i < len(line):
+            ch = line[i]
+            if quote:
+                if ch == "\\":
+                    i += 1
+                elif ch == quote:
+                    quote = None
+            elif ch in "\"'":
+                quote = ch
+            elif line.startswith(line_comment, i):
+                cut = i
+                break
+            i += 1
+        code = line[:cut].rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def attn_source_hash() -> str:
-    """Hash of the attention kernels' source and of the build script (whose flags shape the generated code)."""
+    """Hash of the attention kernels' code and of the build script (whose flags shape the generated code),
+    comments left out: a change to a comment leaves the generated code, and so the profiles taken on it, valid."""
     import hashlib
     h = hashlib.sha256()
-    for rel in (("csrc", "attn_bf16.hip"), ("csrc", "kernels.hpp"), ("build.py",)):
-        with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", *rel), "rb") as f:
-            h.update(f.read())
+    for rel, mark in ((("csrc", "attn_bf16.hip"), "//"), (("csrc", "kernels.hpp"), "//"), (("build.py",), "#")):
+        with open(os.path.join(ROOT, "paged_sliding_window_kv_amd", *rel), encoding="utf-8") as f:
+            h.update(code_text(f.read(), mark).encode())
     return h.hexdigest()[:16]
 
 
@@ -1092,6 +1128,9 @@ def main(argv=None):
         if meas:
             rf["peak_measured"] = meas
             rf["frac_of_measured"] = rf["achieved"] / meas
+        if rf.get("kernel") in ("attn_wide_kernel", "attn_wide_kernel (global)"):
+            rf["tile_mix_tflops"] = probes["tile_mix_tflops"]
+            rf["frac_of_tile_mix"] = rf["achieved"] / probes["tile_mix_tflops"]
     out = {
         "metric": METRIC,
         "value": res["value"],

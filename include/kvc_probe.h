@@ -33,6 +33,19 @@ size_t kvc_probe_scratch_bytes(void);
  * scratch: device buffer of kvc_probe_scratch_bytes. */
 int kvc_probe_mfma_bf16(void* scratch, size_t scratch_bytes, kvc_stream_t stream, double* tflops);
 
+/* The 512-row attention kernel's per-tile instruction mix on its own: per
+ * wave and 64-key tile, the K and V fragment reads from LDS, one workgroup
+ * barrier, 32 products (v_mfma_f32_32x32x16_bf16) and the online softmax of two
+ * 32-row blocks issued as the kernel issues them (each block's exponentials,
+ * FMAs and adds in fenced groups beside the other block's products), with no
+ * global memory, table walk, masks or rare-path checks; eight waves and
+ * 96 KiB of LDS per workgroup, one workgroup per compute unit.  *tflops
+ * receives the products' rate in TFLOP/s: the ceiling that this mix of
+ * matrix and vector work sets for the kernel on this chip ("vLLM-Omni RFC
+ * #2727: Reconstruction Engine", section 2.2: global attention is the compute
+ * bottleneck).  scratch: device buffer of kvc_probe_scratch_bytes. */
+int kvc_probe_tile_mix(void* scratch, size_t scratch_bytes, kvc_stream_t stream, double* tflops);
+
 /* HBM bandwidth: a streaming read of `bytes` from src (16-byte loads folded
  * into one word per thread) and a streaming copy of `bytes` from src to dst.
  * *read_gbs receives bytes / time, *copy_gbs (read + written bytes) / time,

@@ -38,7 +38,7 @@ EXPORTED = (
     "kvc_windowed_keep", "kvc_windowed_drop", "kvc_windowed_get_state",
     "kvc_strerror", "kvc_last_error", "kvc_version", "kvc_set_kernel_events",
     # include/kvc_probe.h
-    "kvc_probe_scratch_bytes", "kvc_probe_mfma_bf16", "kvc_probe_hbm",
+    "kvc_probe_scratch_bytes", "kvc_probe_mfma_bf16", "kvc_probe_tile_mix", "kvc_probe_hbm",
 )
 MAX_INLINE_PAGES = 640
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -153,6 +153,7 @@ def _declare(lib):
         "kvc_set_kernel_events": (C.c_int, [vp, vp]),
         "kvc_probe_scratch_bytes": (C.c_size_t, []),
         "kvc_probe_mfma_bf16": (C.c_int, [vp, C.c_size_t, vp, C.POINTER(C.c_double)]),
+        "kvc_probe_tile_mix": (C.c_int, [vp, C.c_size_t, vp, C.POINTER(C.c_double)]),
         "kvc_probe_hbm": (C.c_int, [vp, vp, C.c_size_t, vp, C.c_size_t, vp, C.POINTER(C.c_double),
                                     C.POINTER(C.c_double)]),
         "kvc_strerror": (C.c_char_p, [C.c_int]),

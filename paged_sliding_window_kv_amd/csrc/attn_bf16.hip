@@ -869,11 +869,11 @@ __global__ __launch_bounds__(NB * 128) void attn_bf16_kernel(const Src src) {
 // ---------------------------------------------------------------------------
 // 256-row tiles: software-pipelined kernel.
 //
-// On CDNA4 a wave's vector (VALU) work overlaps matrix products well only when
-// the same wave issues them interleaved: products that other waves queue on a
-// busy matrix core hold the issue port, so the attn_bf16_kernel layout (each
-// wave: all products of a tile, then its softmax, then the next products)
-// runs products and softmax one after the other.  Here eight waves (two per
+// On CDNA4 a wave's vector (VALU) work overlaps matrix products when the
+// SIMD has both kinds of work to issue at once; in the attn_bf16_kernel layout
+// (each wave: all products of a tile, then its softmax, then the next
+// products) the waves of a SIMD tend to fall into the same phase, and products
+// and softmax then run one after the other.  Here eight waves (two per
 // SIMD, up to 256 registers each) each own 32 query rows of the tile over
 // every key tile, with their queries in registers, and interleave their own
 // instruction streams:
@@ -1608,9 +1608,9 @@ __global__ __launch_bounds__(512) void attn_wide_kernel(const Src src) {
     return tile_sum(s0, s1);
   };
   // One tile with each block's softmax issued beside the other block's
-  // products: a wave's VALU work runs beside matrix products only when the
-  // same wave issues them interleaved, so the tile is laid out as fenced
-  // groups of one product plus a four-element slice of a softmax:
+  // products, so that every wave keeps both the matrix core and the VALU fed
+  // whatever phase the other wave of its SIMD is in: the tile is laid out as
+  // fenced groups of one product plus a four-element slice of a softmax:
   //   block A's 8 score products; 8 x (one of block B's score products, a
   //   slice of block A's softmax); rare path A; block A's probabilities to
   //   bf16 and the V fragments; 8 x (one of block A's P V products, a slice

@@ -57,3 +57,11 @@ def test_chunked_and_global_visible_tokens_match_oracle():
     for _ in range(100):
         og.append()
     assert _visible(og) == 100 * bench.VGGT_TOKENS == 137400
+
+
+def test_profile_hash_ignores_comments_only():
+    """The hash that ties committed counter summaries to the kernel source sees code, not comments."""
+    src = 'int a = 1;  // one\n// a comment line\n\nconst char* s = "x // y";  /* kept */\n'
+    assert bench.code_text(src, "//") == 'int a = 1;\nconst char* s = "x // y";  /* kept */'
+    assert bench.code_text("x = 1  # note\n# only\ny = '#'\n", "#") == "x = 1\ny = '#'"
+    assert bench.code_text("a = 1\n", "//") != bench.code_text("a = 2\n", "//")
