@@ -144,8 +144,18 @@ def test_global_and_frame_attention_full_size_sampled_rows():
         dc.append(to_dev(k, "bf16"), to_dev(v, "bf16"))
     qall = np.concatenate(qs)
     dq = to_dev(qall, "bf16")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
     o, lse = dc.attend(dq)
     torch.cuda.synchronize()
+    # no score matrix is materialised ("vLLM-Omni RFC #2727", section 2.3: at 100
+    # frames one head's scores alone take about 35 GB): the call allocates its
+    # outputs (O 281 MB, lse 8.8 MB) and nothing of the scores' size
+    grown = torch.cuda.max_memory_allocated() - base
+    scores_one_head = (F * T) ** 2 * 2
+    log(f"  attention call peak allocation {grown / 2**20:.1f} MiB (one head's bf16 scores: {scores_one_head / 2**30:.1f} GiB)")
+    assert grown < scores_one_head / 100
     k_all = bits_f64(np.concatenate(ks)).transpose(1, 0, 2)
     v_all = bits_f64(np.concatenate(vs)).transpose(1, 0, 2)
     rng = np.random.default_rng(4)
