@@ -150,8 +150,9 @@ long query_tiles(const paged_attn_args& a) {
 // read back at HBM rate, against one page of a 256-row tile's products).
 // A LingBot frame's 16 tiles get 16 splits (one round); 6 batched streams' 96
 // tiles get 8 (three full rounds) rather than 3 (a full round and a nearly
-// empty one); a 10,992-query chunk's 688 tiles over 172 pages get 4 (eleven
-// rounds, the last nearly full) rather than 1 (three rounds, the last 69% full).
+// empty one); a 10,992-query chunk's 352 tiles of 512 rows over 172 pages get
+// 5 (seven rounds, the last 88% full) rather than 1 (two rounds, the second
+// 38% full); the 137,400-query global call's 4,304 tiles stay unsplit.
 // A split is taken only when it beats one split by 3% in the model.
 int splits_for_pages(const paged_attn_args& a, long tiles, int pages) {
   const long slots = workgroup_slots(a);
@@ -384,8 +385,14 @@ int attend_table(const kvc_t* c, const int32_t* ids, const int32_t* lens, int32_
   h[2 * n + 3] = n;
   int32_t* d = static_cast<int32_t*>(workspace);
   hipError_t e = hipMemcpyAsync(d, h, words * sizeof(int32_t), hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipEventRecord(c->ring.done[slot], st);
   if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+  e = hipEventRecord(c->ring.done[slot], st);
+  if (e != hipSuccess) {
+    // the copy is queued but cannot be tracked: let it finish before the slot
+    // can be written again
+    (void)hipStreamSynchronize(st);
+    return fail(KVC_ERR_DEVICE, "table upload: %s", hipGetErrorString(e));
+  }
   c->ring.in_flight[slot] = true;
   p.page_ids = d;
   p.page_lens = d + n;
