@@ -59,6 +59,34 @@ def test_brute_force():
     assert check_brute_force()
 
 
+def check_library_attention(att=attention_f64) -> bool:
+    """Oracle attention == PyTorch's scaled_dot_product_attention (CPU, float64) for O, and
+    == torch.logsumexp of the scaled scores for lse: library routines that share no code with the
+    oracle.  Shapes span one query to several 1,024-row query blocks of the oracle, uneven key
+    counts, and a row of planted large scores (peaky softmax)."""
+    import torch
+    rng = np.random.default_rng(11)
+    ok = True
+    for lq, lk, h, d, scale in ((1, 7, 2, 8, None), (37, 300, 3, 16, 0.21), (2100, 517, 2, 64, None)):
+        q = rng.standard_normal((lq, h, d))
+        k = rng.standard_normal((h, lk, d))
+        v = rng.standard_normal((h, lk, d))
+        q[0] *= 6.0  # peaky first row
+        o, lse = att(q, k, v, scale)
+        s = (1.0 / math.sqrt(d)) if scale is None else scale
+        tq = torch.from_numpy(q).permute(1, 0, 2)        # [H, Lq, d]
+        tk, tv = torch.from_numpy(k), torch.from_numpy(v)  # [H, Lk, d]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s).permute(1, 0, 2).numpy()
+        ref_lse = torch.logsumexp(s * (tq @ tk.transpose(1, 2)), dim=-1).transpose(0, 1).numpy()
+        ok &= np.allclose(o, ref, rtol=0, atol=1e-12)
+        ok &= np.allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def test_library_attention():
+    assert check_library_attention()
+
+
 def test_closed_forms():
     rng = np.random.default_rng(5)
     h, d, lk = 3, 16, 37
@@ -361,10 +389,22 @@ def test_planted_mistakes_are_caught(monkeypatch):
     def swapped(q, k, v, sm_scale=None, block=1024):
         return attention_f64(q, v, k, sm_scale, block)
     assert not check_brute_force(swapped)
+    assert not check_library_attention(swapped)
     # 2. scale applied twice (dropped/duplicated factor)
     def twice(q, k, v, sm_scale=None, block=1024):
         return attention_f64(q, k, v, (sm_scale or 1.0) ** 2, block)
     assert not check_brute_force(twice)
+    # 2b. default scale 1/d instead of 1/sqrt(d)
+    def wrong_default(q, k, v, sm_scale=None, block=1024):
+        return attention_f64(q, k, v, sm_scale if sm_scale is not None else 1.0 / q.shape[2], block)
+    assert not check_library_attention(wrong_default)
+    # 2c. lse missing the running maximum (log of the shifted sum only)
+    def lse_no_max(q, k, v, sm_scale=None, block=1024):
+        o, lse = attention_f64(q, k, v, sm_scale, block)
+        s = (1.0 / math.sqrt(q.shape[2])) if sm_scale is None else sm_scale
+        m = np.stack([(s * np.einsum('qd,kd->qk', q[:, h], k[h])).max(axis=1) for h in range(k.shape[0])], axis=1)
+        return o, lse - m
+    assert not check_library_attention(lse_no_max)
     # 3. merge that forgets to renormalise
     def bad_merge(parts):
         parts = list(parts)
