@@ -256,7 +256,7 @@ def run_chunked(args) -> dict:
     dev = torch.device("cuda:0")
     lb = lib()
     caches = [KvCache(num_heads=H, dtype=args.kv_dtype, patch_tokens=T, special_tokens=0, num_scale_units=0,
-                      window_units=W, max_units=warm + 2 * steps, device=dev) for _ in range(L)]
+                      window_units=W, max_units=warm + steps, device=dev) for _ in range(L)]
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     bank = 2
@@ -270,14 +270,17 @@ def run_chunked(args) -> dict:
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
     kr = args.keep_ratio
-    clock = CallClock(L)
+    # events around every attention kernel of the timed steps (a 2 ms kernel:
+    # the markers cost 0.1-0.4%), read after the timed region
+    clock = CallClock(L * steps)
 
-    def step(i, timed_calls=False):
+    def step(i, ci=None):
+        """Chunk step i; ci: first clock slot of its 24 attention calls (None: no events)."""
         b = i % bank
         for l in range(L):
             _ok(lb.kvc_append_frame(caches[l].handle, ks[l][b].data_ptr(), vs[l][b].data_ptr(), sp), "append")
-            if timed_calls:
-                clock.before(l)
+            if ci is not None:
+                clock.before(ci + l)
             if kr < 1.0:
                 # AVGGT-style: each layer its own random page subset (seed = layer)
                 _ok(lb.kvc_attend_subset(caches[l].handle, kr, l, 0, 0, qs[l][b].data_ptr(), T, 0.0,
@@ -285,19 +288,18 @@ def run_chunked(args) -> dict:
             else:
                 _ok(lb.kvc_attend(caches[l].handle, qs[l][b].data_ptr(), T, 0.0, out.data_ptr(),
                                   lse.data_ptr(), ws.data_ptr(), wsb, sp), "attend")
-            if timed_calls:
-                clock.after(l)
-        if timed_calls:
-            clock.collect(L)
+            if ci is not None:
+                clock.after(ci + l)
 
     for i in range(warm):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warm + i)
+        step(warm + i, i * L)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    clock.collect(L * steps)
     lk = W * T
     if kr < 1.0:
         # keys each layer attends: the subset keeps the same table positions every steady-state step
@@ -307,9 +309,6 @@ def run_chunked(args) -> dict:
     flops_step = sum(attn_flops(T, x, H) for x in lks)
     kv_e = kv_elem_bytes(args.kv_dtype)
     bytes_call = sum(attn_bytes(T, x, H, kv_elem=kv_e) for x in lks) / L
-    # replay with events around every call (same shapes, full window)
-    for i in range(steps):
-        step(warm + steps + i, timed_calls=True)
     n = clock.calls
     flops_call = flops_step / L
     k_us = clock.kernel_s / n * 1e6
@@ -743,39 +742,42 @@ def run_global(args) -> dict:
         ids, lens = cc.visible_table()
         tabs.append((torch.from_numpy(ids).to(dev), torch.from_numpy(lens).to(dev)))
     torch.cuda.synchronize()
-    clock_g = CallClock(L)
-    clock_f = CallClock(L)
+    # events around every call of the timed passes (77 ms global calls and 1 ms
+    # frame calls: the markers cost well under 1%), read after the timed region
+    clock_g = CallClock(L * steps)
+    clock_f = CallClock(L * steps)
 
-    def one_pass(timed_calls=False):
+    def one_pass(ci=None):
+        """One pass over the 24 layers; ci: first clock slot of its calls (None: no events)."""
+        timed_calls = ci is not None
         for l in range(L):
             cc = caches[l]
             _ok(lb.kvc_reset(cc.handle), "reset")
             for f in range(frames):
                 _ok(lb.kvc_append_frame(cc.handle, k[l].data_ptr() + f * fb, v[l].data_ptr() + f * fb, sp), "append")
             if timed_calls:
-                clock_g.before(l)
+                clock_g.before(ci + l)
             _ok(lb.kvc_attend(cc.handle, q[l].data_ptr(), T, 0.0, out_g.data_ptr(), lse.data_ptr(), ws.data_ptr(),
                               wsb, sp), "attend")
             if timed_calls:
-                clock_g.after(l)
-                clock_f.before(l)
+                clock_g.after(ci + l)
+                clock_f.before(ci + l)
             paged_attention(q[l], cc.k_pool, cc.v_pool, tabs[l][0], tabs[l][1], qo, kv, VGGT_TOKENS, upp, out=out_f,
                             lse=None, workspace=ws)
             if timed_calls:
-                clock_f.after(l)
-        if timed_calls:
-            clock_g.collect(L)
-            clock_f.collect(L)
+                clock_f.after(ci + l)
 
     one_pass()
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated(dev)  # inputs, pools, outputs, workspace: all resident
     torch.cuda.reset_peak_memory_stats(dev)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        one_pass()
+    for i in range(steps):
+        one_pass(i * L)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    clock_g.collect(L * steps)
+    clock_f.collect(L * steps)
     peak = torch.cuda.max_memory_allocated(dev)
     score_bytes = T * T * 2  # the score matrix one head would need if it were stored (bf16)
     log(f"[bench] global: device memory {base / 2**30:.2f} GiB before the pass, peak {peak / 2**30:.2f} GiB during it "
@@ -783,10 +785,9 @@ def run_global(args) -> dict:
     fl_g = L * attn_flops(T, T, H)
     fl_f = L * frames * attn_flops(VGGT_TOKENS, VGGT_TOKENS, H)
     tf = steps * (fl_g + fl_f) / el / 1e12
-    one_pass(timed_calls=True)
-    kg = clock_g.kernel_s / L
+    kg = clock_g.kernel_s / clock_g.calls
     ach = fl_g / L / kg / 1e12
-    tfr = clock_f.call_s / L
+    tfr = clock_f.call_s / clock_f.calls
     log(f"[bench] global: {el / steps:.3f} s/pass, {tf:.1f} TFLOP/s overall; global kernel {kg * 1e3:.2f} ms avg "
         f"({ach:.1f} TFLOP/s, {ach / PEAK_BF16_TFLOPS:.1%} of bf16 peak); frame calls {tfr * 1e3:.2f} ms avg "
         f"({fl_f / L / tfr / 1e12:.1f} TFLOP/s)")
@@ -802,7 +803,7 @@ def run_global(args) -> dict:
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "attn_wide_kernel (global)",
                      "per_launch_flops": fl_g / L, "avg_kernel_us": kg * 1e6,
-                     "avg_call_us_with_merge": clock_g.call_s / L * 1e6, "calls": L,
+                     "avg_call_us_with_merge": clock_g.call_s / clock_g.calls * 1e6, "calls": clock_g.calls,
                      "frame_attn_tflops": fl_f / L / tfr / 1e12},
     }
     if not args.no_cpu_baseline:
