@@ -23,7 +23,10 @@ Other workloads (--workload): "stream" (the LingBot stream as the main line;
 attention over 100 frames x 1374 tokens, then per-frame attention),
 "stream_batched" (--batch LingBot streams, one attention launch per layer and
 frame), "keyframe" (a small fp32 stream over 10,000 frames that keeps every
-fourth frame and rolls the others back).
+fourth frame and rolls the others back), "windowed" (the LingBot stream in
+windowed mode, section 4: 25,000 frames, a keyframe every second frame, the
+24 caches restarted once per window of 128 kept units with the last 16
+shared).
 
 Every workload reports `roofline` for its dominant kernel (algorithmic FLOPs
 or bytes per launch over the kernel's own duration, taken with HIP events on
@@ -55,6 +58,8 @@ VGGT_TOKENS = 1374
 CHUNK = dict(layers=24, heads=16, d=64, page=256, frames_per_chunk=8, window_chunks=4)
 STREAM = dict(layers=24, heads=16, d=64, page=256, patch=256, special=6, scale=8, window=64, frames=1000)
 KEYFRAME = dict(heads=4, d=64, page=256, patch=256, special=6, scale=2, window=4, interval=4, frames=10000)
+WINDOWED = dict(layers=24, heads=16, d=64, page=256, patch=256, special=6, scale=8, window=64, slots=128, overlap=16,
+                interval=2, frames=25000)
 GLOBAL = dict(layers=24, heads=16, d=64, frames=100)
 
 
@@ -964,6 +969,237 @@ def run_keyframe(args) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# Windowed stream (bf16)
+# ----------------------------------------------------------------------------
+def windowed_schedule(frames: int, c=WINDOWED):
+    """Per frame t: (units in the cache when frame t attends, whether its append restarted the window).
+
+    A window holds c["slots"] kept units; the append after the window is full
+    resets the cache and re-appends the last c["overlap"] kept units (fewer if
+    fewer were ever kept); a frame that is not a keyframe is rolled back and
+    takes no slot.
+    """
+    units = slots = kept = 0
+    out = []
+    for t in range(frames):
+        restart = slots >= c["slots"]
+        if restart:
+            units = slots = min(kept, c["overlap"])
+        units += 1
+        out.append((units, restart))
+        if keyframe_kept(t, c):
+            slots += 1
+            kept += 1
+        else:
+            units -= 1
+    return out
+
+
+def oracle_windowed_sample(sample: int, seed: int = 0):
+    """The oracle on `sample` frames of one layer of the windowed stream, centred on the first restart.
+
+    Frames before the sample are appended, kept or dropped untimed; each
+    timed frame is appended (with the restart when it falls there), gathered,
+    attended in fp64 and kept or dropped.  Returns (seconds, flops, first
+    timed frame).
+    """
+    import synth
+    from oracle import OracleCache, OracleConfig, OracleWindowed, attention_f64, to_f64
+    c = WINDOWED
+    tok = c["patch"] + c["special"]
+    first = next(t for t, (_, r) in enumerate(windowed_schedule(4 * c["slots"] * c["interval"])) if r)
+    t0_ = max(0, first - sample // 2)
+    ow = OracleWindowed(OracleCache(OracleConfig(num_heads=c["heads"], head_dim=c["d"], page_size=c["page"],
+                                                 patch_tokens=c["patch"], special_tokens=c["special"],
+                                                 num_scale_units=c["scale"], window_units=c["window"],
+                                                 max_units=c["slots"] + 1, store_dtype="bf16")),
+                        c["slots"], c["overlap"])
+    bank = [synth.frame_qkv(seed, 0, i, tok, c["heads"], c["d"], "bf16") for i in range(4)]
+
+    def finish(t):
+        if keyframe_kept(t, c):
+            ow.keep()
+        else:
+            ow.drop()
+
+    for t in range(t0_):
+        _, k, v = bank[t % 4]
+        ow.append(k, v)
+        finish(t)
+    fl = 0.0
+    start = time.perf_counter()
+    for t in range(t0_, t0_ + sample):
+        q, k, v = bank[t % 4]
+        ow.append(k, v)
+        gk, gv = ow.cache.gather()
+        attention_f64(to_f64(q), to_f64(gk), to_f64(gv))
+        fl += attn_flops(tok, gk.shape[1], c["heads"], c["d"])
+        finish(t)
+    return time.perf_counter() - start, fl, t0_
+
+
+def run_windowed(args) -> dict:
+    """Windowed LingBot stream: 24 layer caches restarted once per window of 128 kept units, 16 units shared.
+
+    Per frame and layer: kvc_windowed_append (the restart, when the window is
+    full, inside it), the frame's attention, then kvc_windowed_keep (keyframes:
+    the unit takes a slot and is copied into the overlap ring) or
+    kvc_windowed_drop (rollback).  The step is one frame through 24 layers.
+    """
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, lib
+    from paged_sliding_window_kv_amd._lib import KvcWindowedState
+    c = WINDOWED
+    frames, layers, H, d = args.steps, c["layers"], c["heads"], c["d"]
+    tok = c["patch"] + c["special"]
+    log(f"[bench] windowed: {layers} layers x {frames} frames, window {c['slots']} slots, overlap {c['overlap']}, "
+        f"keyframe every {c['interval']} frames, warmup {args.warmup}")
+    dev = torch.device("cuda:0")
+    L = lib()
+    caches = [KvCache(num_heads=H, head_dim=d, page_size=c["page"], dtype="bf16", patch_tokens=c["patch"],
+                      special_tokens=c["special"], num_scale_units=c["scale"], window_units=c["window"],
+                      max_units=c["slots"] + 1, device=dev) for _ in range(layers)]
+    nb = C.c_size_t()
+    _ok(L.kvc_windowed_ring_bytes(caches[0].handle, c["overlap"], C.byref(nb)), "kvc_windowed_ring_bytes")
+    rings = [[torch.empty(nb.value, dtype=torch.uint8, device=dev) for _ in range(2)] for _ in range(layers)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bank = 4
+    shp = (bank, tok, H, d)
+    q, k, v = ([torch.randn(shp, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                for _ in range(layers)] for _ in range(3))
+    o = [torch.empty((tok, H, d), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+    lse = [torch.empty((tok, H), dtype=torch.float32, device=dev) for _ in range(layers)]
+    wsb = caches[0].workspace_bytes(tok)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    fb = tok * H * d * 2
+    qp = [[q[l].data_ptr() + i * fb for i in range(bank)] for l in range(layers)]
+    kp = [[k[l].data_ptr() + i * fb for i in range(bank)] for l in range(layers)]
+    vp = [[v[l].data_ptr() + i * fb for i in range(bank)] for l in range(layers)]
+    op, lp, wsp = [x.data_ptr() for x in o], [x.data_ptr() for x in lse], ws.data_ptr()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    handles = []
+
+    def start():
+        """Fresh windowed handles over emptied caches (the rings are reused)."""
+        torch.cuda.synchronize()
+        for h in handles:
+            _ok(L.kvc_windowed_destroy(h), "kvc_windowed_destroy")
+        handles.clear()
+        for l, cc in enumerate(caches):
+            cc.reset()
+            h = C.c_void_p()
+            _ok(L.kvc_windowed_create(cc.handle, c["slots"], c["overlap"], rings[l][0].data_ptr(),
+                                      rings[l][1].data_ptr(), C.byref(h)), "kvc_windowed_create")
+            handles.append(h)
+        torch.cuda.synchronize()
+
+    restarted = C.c_int32()
+    rp = C.byref(restarted)
+    app, att, keep, drop = L.kvc_windowed_append, L.kvc_attend, L.kvc_windowed_keep, L.kvc_windowed_drop
+
+    def frame(t, clock=None):
+        b = t % bank
+        kf = keyframe_kept(t, c)
+        for l in range(layers):
+            s = app(handles[l], kp[l][b], vp[l][b], sp, rp)
+            if s:
+                _ok(s, "kvc_windowed_append")
+            if clock is not None:
+                clock.before(l)
+            s = att(caches[l].handle, qp[l][b], tok, 0.0, op[l], lp[l], wsp, wsb, sp)
+            if s:
+                _ok(s, "kvc_attend")
+            if clock is not None:
+                clock.after(l)
+            s = keep(handles[l], sp) if kf else drop(handles[l])
+            if s:
+                _ok(s, "kvc_windowed_keep/drop")
+        if clock is not None:
+            clock.collect(layers)
+
+    try:
+        start()
+        for t in range(args.warmup):
+            frame(t)
+        start()
+        mem0 = torch.cuda.memory_allocated(dev)
+        t0 = time.perf_counter()
+        for t in range(frames):
+            frame(t)
+            if (t + 1) % 5000 == 0:
+                log(f"[bench] windowed: frame {t + 1}")
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        mem1 = torch.cuda.memory_allocated(dev)
+        sched = windowed_schedule(frames)
+        st = KvcWindowedState()
+        _ok(L.kvc_windowed_get_state(handles[0], C.byref(st)), "kvc_windowed_get_state")
+        restarts = sum(r for _, r in sched)
+        kept = sum(keyframe_kept(t, c) for t in range(frames))
+        assert st.windows == restarts, (st.windows, restarts)
+        assert caches[0].state()["num_units"] == sched[-1][0] - (0 if keyframe_kept(frames - 1, c) else 1)
+        assert mem1 == mem0, (mem0, mem1)
+        lks = [keyframe_lk(u, c) for u, _ in sched]
+        total_flops = layers * sum(attn_flops(tok, lk, H, d) for lk in lks)
+        tflops = total_flops / elapsed / 1e12
+        fps = frames / elapsed
+        log(f"[bench] windowed: {frames} frames in {elapsed:.3f} s: {fps:.1f} frames/s, {tflops:.1f} TFLOP/s; "
+            f"{restarts} restarts, {kept} units kept, device memory unchanged")
+        # attention calls alone: the first `replay` frames again, events around every call
+        replay = min(frames, args.replay_frames)
+        start()
+        clock = CallClock(layers)
+        for t in range(replay):
+            frame(t, clock)
+        byt = layers * sum(attn_bytes(tok, lk, H) for lk in lks[:replay])
+        flo = layers * sum(attn_flops(tok, lk, H, d) for lk in lks[:replay])
+        n = clock.calls
+        k_us, c_us = clock.kernel_s / n * 1e6, clock.call_s / n * 1e6
+        ach_gbs = byt / clock.kernel_s / 1e9
+        log(f"[bench] windowed attention over frames 0..{replay - 1}: kernel {k_us:.2f} us avg "
+            f"({ach_gbs:.0f} GB/s), call with merge {c_us:.2f} us")
+    finally:
+        torch.cuda.synchronize()
+        for h in handles:
+            L.kvc_windowed_destroy(h)
+        handles.clear()
+    res = {
+        "value": tflops, "unit": "TFLOP/s", "ms_per_step": elapsed / frames * 1e3, "frames_per_s": fps,
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "dtype": "bf16",
+        "config": {"workload": f"windowed_stream: {layers} layer caches, {H} heads x {d}, bf16, 256 patch + 6 "
+                               f"special tokens/frame, {c['scale']} scale frames, {c['window']}-frame window, "
+                               f"restart every {c['slots']} kept units sharing the last {c['overlap']}, keyframe "
+                               f"every {c['interval']} frames (others rolled back), 262 queries/step, {frames} "
+                               "frames; step = one frame through 24 layers (windowed append, attention, keep or "
+                               "drop)",
+                   "layers": layers, "heads": H, "head_dim": d, "page_size": c["page"], "frames": frames,
+                   "window_slots": c["slots"], "overlap": c["overlap"], "keyframe_interval": c["interval"],
+                   "restarts": restarts, "units_kept": kept, "max_visible_tokens": max(lks),
+                   "mean_visible_tokens": sum(lks) / len(lks),
+                   "kv_pool_mib_per_layer": caches[0].k_pool.numel() * caches[0].k_pool.element_size() * 2 / 2**20,
+                   "ring_mib_per_layer": 2 * nb.value / 2**20,
+                   "device_memory_growth_bytes": mem1 - mem0},
+        "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "attn_bf16_kernel (272-row tile)",
+                     "per_launch_bytes": byt / n, "per_launch_flops": flo / n, "avg_kernel_us": k_us,
+                     "avg_call_us_with_merge": c_us, "calls": n, "replayed_frames": replay,
+                     "kernel_tflops": flo / clock.kernel_s / 1e12},
+    }
+    if not args.no_cpu_baseline and args.cpu_sample > 0:
+        sample = args.cpu_sample
+        log(f"[bench] oracle sample: 1 layer, {sample} frames around the first restart")
+        sec, fl, first = oracle_windowed_sample(sample)
+        ot = fl / sec / 1e12
+        res["cpu_baseline"] = cpu_baseline(
+            ot, "TFLOP/s",
+            f"1 of 24 layers, frames {first}..{first + sample - 1} of the windowed stream (windowed append with "
+            f"the first restart, gather, fp64 attention, keep or drop), {sec:.1f} s; frames/s scaled to 24 layers",
+            sec, {"frames_per_s": 1.0 / (sec / sample * layers)})
+    return res
+
+
+# ----------------------------------------------------------------------------
 # counter calibration and profile bookkeeping
 # ----------------------------------------------------------------------------
 def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -1048,7 +1284,7 @@ def add_traffic(res: dict, summary: str) -> None:
 
 
 DEFAULT_STEPS = {"chunked": 20, "stream": STREAM["frames"], "global": 1, "stream_batched": STREAM["frames"],
-                 "keyframe": KEYFRAME["frames"]}
+                 "keyframe": KEYFRAME["frames"], "windowed": WINDOWED["frames"]}
 
 
 def parse_args(argv=None):
@@ -1057,10 +1293,10 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps: chunk steps at the full window (chunked, default 20), the last K frames of "
                          "the 1,000-frame stream (stream, stream_batched), passes (global, default 1), frames "
-                         "(keyframe, default 10,000)")
+                         "(keyframe, default 10,000; windowed, default 25,000)")
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps before timing (chunked: at least 4)")
     ap.add_argument("--workload", default="chunked",
-                    choices=["chunked", "stream", "global", "stream_batched", "keyframe"])
+                    choices=["chunked", "stream", "global", "stream_batched", "keyframe", "windowed"])
     ap.add_argument("--batch", type=int, default=6, help="streams of the stream_batched workload (at most 6 keep "
                     "the 1000-frame tables within one launch)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
@@ -1073,7 +1309,11 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="chunked/global oracle slice: query rows of one layer (all heads)")
-    ap.add_argument("--cpu-sample", type=int, default=24, help="stream oracle sample: last frames of one layer")
+    ap.add_argument("--cpu-sample", type=int, default=24,
+                    help="stream / windowed oracle sample: frames of one layer (the last ones; windowed: around "
+                         "the first restart)")
+    ap.add_argument("--replay-frames", type=int, default=2000,
+                    help="windowed: frames replayed with events around every attention call")
     args = ap.parse_args(argv)
     if args.steps is None:
         args.steps = DEFAULT_STEPS[args.workload]
@@ -1081,6 +1321,8 @@ def parse_args(argv=None):
         ap.error("--steps must be at least 1")
     if args.warmup < 0:
         ap.error("--warmup must be non-negative")
+    if args.replay_frames < 1:
+        ap.error("--replay-frames must be at least 1")
     return args
 
 
@@ -1118,6 +1360,8 @@ def main(argv=None):
         res = run_stream_batched(args)
     elif args.workload == "keyframe":
         res = run_keyframe(args)
+    elif args.workload == "windowed":
+        res = run_windowed(args)
     else:
         res = run_global(args)
     probes = None

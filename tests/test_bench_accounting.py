@@ -65,3 +65,24 @@ def test_profile_hash_ignores_comments_only():
     assert bench.code_text(src, "//") == 'int a = 1;\nconst char* s = "x // y";  /* kept */'
     assert bench.code_text("x = 1  # note\n# only\ny = '#'\n", "#") == "x = 1\ny = '#'"
     assert bench.code_text("a = 1\n", "//") != bench.code_text("a = 2\n", "//")
+
+
+def test_windowed_schedule_matches_the_c_driver():
+    """Windowed stream: bench's per-frame unit count and restart flag follow libkvc's windowed driver on a
+    host-only cache of the benched shape, and a frame attends to keyframe_lk(units) tokens."""
+    from paged_sliding_window_kv_amd import KvCache, WindowedStream
+    c = bench.WINDOWED
+    frames = 1200
+    hc = KvCache(num_heads=1, patch_tokens=c["patch"], special_tokens=c["special"], num_scale_units=c["scale"],
+                 window_units=c["window"], max_units=c["slots"] + 1)
+    ws = WindowedStream(hc, c["slots"], c["overlap"])
+    sched = bench.windowed_schedule(frames)
+    for t, (units, restart) in enumerate(sched):
+        assert ws.append() == restart, t
+        assert hc.state()["num_units"] == units, t
+        assert int(hc.visible_table()[1].sum()) == bench.keyframe_lk(units, c), t
+        if bench.keyframe_kept(t, c):
+            ws.keep()
+        else:
+            ws.drop()
+    assert ws.windows == sum(r for _, r in sched) >= 4

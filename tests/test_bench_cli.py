@@ -37,8 +37,8 @@ def test_chunked_oracle_leg_runs():
 
 
 def test_stream_oracle_leg_with_driver_arguments():
-    """The stream extra's cpu_baseline leg at its default sample (the round-1 crash: a sample larger than
-    the frames streamed).  Sizes the oracle cache for every frame it appends."""
+    """The stream extra's cpu_baseline leg at its default sample (a regression test for a sample larger
+    than the frames streamed).  Sizes the oracle cache for every frame it appends."""
     a = bench.parse_args(["--gpus", "1", "--steps", "20", "--warmup", "5"])
     sec, flops, n = bench.oracle_stream_sample(bench.STREAM["frames"], a.cpu_sample)
     assert n == a.cpu_sample and sec > 0
@@ -52,3 +52,17 @@ def test_host_info_names_cores_and_blas():
     h = bench.host_info()
     assert h["cores"] >= 1 and h["blas_threads"] >= 1
     assert h["cpu_model"] and h["blas"]
+
+
+def test_windowed_arguments_and_oracle_leg():
+    """--workload windowed: 25,000 frames by default (the pages' long indoor run); the oracle leg times
+    frames around the first restart, which falls where the 129th kept unit is appended."""
+    a = bench.parse_args(["--workload", "windowed"])
+    assert a.steps == 25000 and a.replay_frames == 2000
+    c = bench.WINDOWED
+    sched = bench.windowed_schedule(600)
+    first = next(t for t, (_, r) in enumerate(sched) if r)
+    assert sum(bench.keyframe_kept(t, c) for t in range(first)) == c["slots"]
+    sec, flops, t0 = bench.oracle_windowed_sample(4)
+    assert t0 == first - 2 and sec > 0
+    assert flops == sum(bench.attn_flops(262, bench.keyframe_lk(sched[t][0], c), 16) for t in range(t0, t0 + 4))
