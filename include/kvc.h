@@ -394,8 +394,10 @@ int kvc_attend_noalloc(const kvc_t* cache, const void* q, int32_t num_q, float s
  * resets the cache and re-appends the last `overlap` kept units of the
  * finished window, oldest first, with the K/V they were appended with; a
  * dropped unit (keyframe skip, section 3) takes no slot.  The K/V of the last
- * `overlap` kept units wait in two caller-owned device rings, so device
- * memory stays fixed however long the stream runs.
+ * `overlap` kept units wait in two caller-owned device rings of overlap + 1
+ * units, so device memory stays fixed however long the stream runs: each
+ * windowed append also writes its unit's K/V into the rings' free slot, in
+ * the same launch as the page scatter.
  *
  * A windowed handle drives one cache; while it exists, append, roll back and
  * reset that cache only through it (attention calls on the cache are fine).
@@ -409,10 +411,10 @@ typedef struct kvc_windowed_state {
   int32_t pending;     /* 1 if an appended unit waits for keep or drop */
 } kvc_windowed_state;
 
-/* Bytes of each ring (K and V) for `overlap` units of this cache:
- * overlap * (patch_tokens + special_tokens) * H * d * activation element
- * size (bf16 for bf16 and FP8 caches, fp32 for fp32 caches); 0 for a
- * host-only cache. */
+/* Bytes of each ring (K and V) for `overlap` shared units of this cache:
+ * (overlap + 1) * (patch_tokens + special_tokens) * H * d * activation
+ * element size (bf16 for bf16 and FP8 caches, fp32 for fp32 caches); 0 when
+ * overlap is 0 or the cache is host-only. */
 int kvc_windowed_ring_bytes(const kvc_t* cache, int32_t overlap, size_t* bytes);
 
 /* Windowed driver over `cache`.  1 <= window_slots, 0 <= overlap <
@@ -427,15 +429,17 @@ int kvc_windowed_destroy(kvc_windowed_t* w);
 /* Append one unit (K/V as kvc_append_frame takes them).  When the window is
  * full, first restarts it as described above; *restarted (nullable) is set to
  * 1 then, else 0.  The unit then waits for kvc_windowed_keep or
- * kvc_windowed_drop, and k_unit / v_unit must hold their data until that call
- * is enqueued on the stream (keep copies them into the ring).  Errors:
+ * kvc_windowed_drop.  The append reads k_unit / v_unit in its own launch on
+ * `stream` (the page scatter and the ring copy), as kvc_append_frame does.
+ * Errors:
  * KVC_ERR_INVALID_ARGUMENT while a unit is waiting; if a restart fails on
  * the device, KVC_ERR_DEVICE and the windowed handle refuses every later
  * append (the cache is then part-way through a restart). */
 int kvc_windowed_append(kvc_windowed_t* w, const void* k_unit, const void* v_unit, kvc_stream_t stream,
                         int32_t* restarted);
-/* The waiting unit is a keyframe: it stays, takes one slot, and its K/V are
- * copied into the ring on `stream` (when overlap > 0). */
+/* The waiting unit is a keyframe: it stays and takes one slot; the ring slot
+ * its append wrote becomes one of the last `overlap` kept units.  Host-only
+ * (no device work; `stream` is unused). */
 int kvc_windowed_keep(kvc_windowed_t* w, kvc_stream_t stream);
 /* The waiting unit is not kept ("LingBot-Map Paged KV Cache", section 3):
  * it is rolled back and takes no slot. */

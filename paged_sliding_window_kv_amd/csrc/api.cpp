@@ -589,47 +589,56 @@ int kvc_destroy(kvc_t* cache) {
 }
 
 int kvc_append_frame(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream) {
-  return guarded("kvc_append_frame", [&] {
-    if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
-    const bool device = c->k_pool != nullptr;
-    if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
-    if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
-    if ((reinterpret_cast<uintptr_t>(k_unit) | reinterpret_cast<uintptr_t>(v_unit)) & 15)
-      return fail(KVC_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
-    if (!device) {
-      const int s = c->pc.append();
-      return s == KVC_OK ? s : fail(s, "append needs %d pages", c->pc.unit_pages());
-    }
-    // plan, launch, then commit: a failed launch leaves the cache unchanged
-    kvc::AppendPlan plan;
-    kvc::AppendParams p{};
-    if (int s = c->pc.plan(&plan, p.unit_pages)) return fail(s, "append needs %d pages", c->pc.unit_pages());
-    const kvc_config& cfg = c->pc.config();
-    p.k_src = k_unit;
-    p.v_src = v_unit;
-    p.k_pool = c->k_pool;
-    p.v_pool = c->v_pool;
-    p.num_heads = cfg.num_heads;
-    p.page_size = cfg.page_size;
-    p.patch_tokens = cfg.patch_tokens;
-    p.special_tokens = cfg.special_tokens;
-    p.special_page0 = plan.special_page0;
-    p.special_slot0 = plan.special_slot0;
-    p.special_count0 = plan.special_count0;
-    p.special_page1 = plan.special_page1;
-    p.num_unit_pages = plan.num_unit_pages;
-    if (cfg.dtype == KVC_DTYPE_FP8_E4M3) {
-      // row exponents follow the codes in each pool buffer
-      const size_t codes = static_cast<size_t>(c->pc.num_pages()) * cfg.num_heads * cfg.page_size * cfg.head_dim;
-      p.k_exp = static_cast<char*>(c->k_pool) + codes;
-      p.v_exp = static_cast<char*>(c->v_pool) + codes;
-    }
-    const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
-    c->pc.commit();
-    return static_cast<int>(KVC_OK);
-  });
+  return guarded("kvc_append_frame", [&] { return kvc::append_unit(c, k_unit, v_unit, stream, nullptr, nullptr); });
 }
+
+}  // extern "C"
+
+int kvc::append_unit(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream, void* k_copy,
+                     void* v_copy) {
+  if (!c) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
+  const bool device = c->k_pool != nullptr;
+  if (device && (!k_unit || !v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "device cache needs K and V");
+  if (!device && (k_unit || v_unit)) return fail(KVC_ERR_INVALID_ARGUMENT, "host-only cache takes NULL K and V");
+  if ((reinterpret_cast<uintptr_t>(k_unit) | reinterpret_cast<uintptr_t>(v_unit)) & 15)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "K and V must be 16-byte aligned");
+  if (!device) {
+    const int s = c->pc.append();
+    return s == KVC_OK ? s : fail(s, "append needs %d pages", c->pc.unit_pages());
+  }
+  // plan, launch, then commit: a failed launch leaves the cache unchanged
+  kvc::AppendPlan plan;
+  kvc::AppendParams p{};
+  if (int s = c->pc.plan(&plan, p.unit_pages)) return fail(s, "append needs %d pages", c->pc.unit_pages());
+  const kvc_config& cfg = c->pc.config();
+  p.k_src = k_unit;
+  p.v_src = v_unit;
+  p.k_pool = c->k_pool;
+  p.v_pool = c->v_pool;
+  p.num_heads = cfg.num_heads;
+  p.page_size = cfg.page_size;
+  p.patch_tokens = cfg.patch_tokens;
+  p.special_tokens = cfg.special_tokens;
+  p.special_page0 = plan.special_page0;
+  p.special_slot0 = plan.special_slot0;
+  p.special_count0 = plan.special_count0;
+  p.special_page1 = plan.special_page1;
+  p.num_unit_pages = plan.num_unit_pages;
+  p.k_copy = k_copy;
+  p.v_copy = v_copy;
+  if (cfg.dtype == KVC_DTYPE_FP8_E4M3) {
+    // row exponents follow the codes in each pool buffer
+    const size_t codes = static_cast<size_t>(c->pc.num_pages()) * cfg.num_heads * cfg.page_size * cfg.head_dim;
+    p.k_exp = static_cast<char*>(c->k_pool) + codes;
+    p.v_exp = static_cast<char*>(c->v_pool) + codes;
+  }
+  const hipError_t e = kvc::launch_kv_append(p, cfg.dtype, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  c->pc.commit();
+  return static_cast<int>(KVC_OK);
+}
+
+extern "C" {
 
 int kvc_rollback_last_frame(kvc_t* c) {
   return guarded("kvc_rollback_last_frame", [&] {

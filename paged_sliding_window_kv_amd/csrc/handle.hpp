@@ -66,6 +66,10 @@ int guarded(const char* where, F&& body) noexcept {
 int attend_fixed_workspace(const kvc_t* c, const void* q, int32_t num_q, float sm_scale, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, kvc_stream_t stream);
 
+// kvc_append_frame's body; k_copy / v_copy (both or neither, device caches
+// only) also receive the unit's K/V activations unchanged, in the same launch.
+int append_unit(kvc_t* c, const void* k_unit, const void* v_unit, kvc_stream_t stream, void* k_copy, void* v_copy);
+
 // Element bytes of appended K/V activations (FP8 caches take bf16).
 inline size_t activation_bytes(int dtype) { return dtype == KVC_DTYPE_F32 ? 4 : 2; }
 

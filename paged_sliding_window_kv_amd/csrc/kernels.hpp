@@ -38,6 +38,8 @@ struct AppendParams {
   int32_t num_unit_pages;
   void* k_exp;            // FP8 caches: row exponents [pages][H][P] (int8), after the codes
   void* v_exp;
+  void* k_copy;           // null, or [T][H][d] activations: the unit's K/V rows as read, copied here too
+  void* v_copy;
   int32_t unit_pages[kMaxUnitPages];
 };
 

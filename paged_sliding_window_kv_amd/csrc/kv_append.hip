@@ -12,7 +12,9 @@
 // transposed in the pool ([dim][slot] per page and head) so that the
 // attention kernel reads it as the row operand of its P*V product; the tile
 // goes through LDS and leaves as 16-byte runs of 8 (bf16) or 4 (fp32)
-// consecutive slots.
+// consecutive slots.  When AppendParams::k_copy is set (windowed mode), every
+// K and V chunk read is also written unchanged to the copy buffers, at its
+// source offset.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -80,8 +82,13 @@ __global__ __launch_bounds__(append_threads<T>()) void kv_append_kernel(const Ap
     const size_t src = (static_cast<size_t>(tok) * H + h) * D + ch * VEC;
     const Dest dd = dest_of(p, tok);
     const size_t dst = ((static_cast<size_t>(dd.page) * H + h) * P + dd.slot) * D + ch * VEC;
-    *reinterpret_cast<V16*>(kpool + dst) = *reinterpret_cast<const V16*>(ksrc + src);
+    const V16 k = *reinterpret_cast<const V16*>(ksrc + src);
     const V16 v = *reinterpret_cast<const V16*>(vsrc + src);
+    *reinterpret_cast<V16*>(kpool + dst) = k;
+    if (p.k_copy) {  // workgroup-uniform
+      *reinterpret_cast<V16*>(static_cast<T*>(p.k_copy) + src) = k;
+      *reinterpret_cast<V16*>(static_cast<T*>(p.v_copy) + src) = v;
+    }
     const T* ve = reinterpret_cast<const T*>(&v);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) vt[t][ch * VEC + e] = ve[e];
@@ -180,7 +187,13 @@ __global__ __launch_bounds__(kFp8Threads) void kv_append_fp8_kernel(const Append
     const uint16_t* src = static_cast<const uint16_t*>(is_v ? p.v_src : p.k_src) +
                           (static_cast<size_t>(tok) * H + h) * D + lane8 * 8;
     uint4 raw = {0u, 0u, 0u, 0u};
-    if (valid) raw = *reinterpret_cast<const uint4*>(src);
+    if (valid) {
+      raw = *reinterpret_cast<const uint4*>(src);
+      if (p.k_copy) {  // the row as read, into the copy at the same offset
+        const size_t off = (static_cast<size_t>(tok) * H + h) * D + lane8 * 8;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(is_v ? p.v_copy : p.k_copy) + off) = raw;
+      }
+    }
     float x[8];
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll

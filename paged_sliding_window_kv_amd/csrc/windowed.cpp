@@ -10,7 +10,11 @@
 // first, with the K/V they were appended with.  Units that are dropped (a
 // keyframe skip rolls them back) take no slot.  The K/V of the last `overlap`
 // kept units wait in a caller-owned device ring, so device memory stays fixed
-// however long the stream runs.
+// however long the stream runs.  The ring has one slot more than `overlap`:
+// every windowed append writes its unit's K/V into the free slot in the same
+// launch that scatters them into pages, and keeping the unit only advances
+// the ring (no copy of its own), while a dropped unit's slot is simply written
+// again by the next append.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -27,16 +31,14 @@ struct kvc_windowed {
   kvc_t* cache = nullptr;
   int32_t window_slots = 0;
   int32_t overlap = 0;
-  char* k_ring = nullptr;  // device [overlap][unit tokens][H][d] activations, or null (host-only cache)
+  char* k_ring = nullptr;  // device [overlap + 1][unit tokens][H][d] activations, or null (host-only cache)
   char* v_ring = nullptr;
   size_t unit_bytes = 0;
   int32_t slots = 0;       // kept units in the current window
   int32_t windows = 0;     // restarts so far
   int32_t ring_len = 0;    // kept units in the ring (at most overlap)
-  int32_t ring_head = 0;   // next ring slot to write
+  int32_t ring_head = 0;   // the free slot: the next append's K/V go here
   bool pending = false;    // an appended unit waits for keep or drop
-  const void* pending_k = nullptr;
-  const void* pending_v = nullptr;
   bool broken = false;     // a restart failed part-way on the device
 };
 
@@ -47,11 +49,14 @@ size_t unit_activation_bytes(const kvc_config& c) {
          kvc::activation_bytes(c.dtype);
 }
 
+int32_t ring_slots(const kvc_windowed* w) { return w->overlap > 0 ? w->overlap + 1 : 0; }
+
 // Restart: reset the cache and re-append the ring's units, oldest first.
 int restart(kvc_windowed* w, kvc_stream_t stream) {
   if (int s = kvc_reset(w->cache)) return s;
+  const int32_t r = ring_slots(w);
   for (int32_t j = 0; j < w->ring_len; ++j) {
-    const int32_t slot = ((w->ring_head - w->ring_len + j) % w->overlap + w->overlap) % w->overlap;
+    const int32_t slot = ((w->ring_head - w->ring_len + j) % r + r) % r;
     const void* k = w->k_ring ? w->k_ring + slot * w->unit_bytes : nullptr;
     const void* v = w->v_ring ? w->v_ring + slot * w->unit_bytes : nullptr;
     if (int s = kvc_append_frame(w->cache, k, v, stream)) {
@@ -71,7 +76,8 @@ extern "C" {
 int kvc_windowed_ring_bytes(const kvc_t* cache, int32_t overlap, size_t* bytes) {
   return guarded("kvc_windowed_ring_bytes", [&] {
     if (!cache || !bytes || overlap < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "bad argument");
-    *bytes = cache->k_pool ? static_cast<size_t>(overlap) * unit_activation_bytes(cache->pc.config()) : 0;
+    const size_t slots = overlap > 0 ? static_cast<size_t>(overlap) + 1 : 0;
+    *bytes = cache->k_pool ? slots * unit_activation_bytes(cache->pc.config()) : 0;
     return static_cast<int>(KVC_OK);
   });
 }
@@ -132,28 +138,29 @@ int kvc_windowed_append(kvc_windowed_t* w, const void* k_unit, const void* v_uni
       if (int s = restart(w, stream)) return s;
       if (restarted) *restarted = 1;
     }
-    if (int s = kvc_append_frame(w->cache, k_unit, v_unit, stream)) return s;
+    // the unit's K/V also go to the ring's free slot, in the append's own launch
+    char* kc = nullptr;
+    char* vc = nullptr;
+    if (w->overlap > 0 && w->k_ring) {
+      const size_t off = static_cast<size_t>(w->ring_head) * w->unit_bytes;
+      kc = w->k_ring + off;
+      vc = w->v_ring + off;
+    }
+    if (int s = kvc::append_unit(w->cache, k_unit, v_unit, stream, kc, vc)) return s;
     w->pending = true;
-    w->pending_k = k_unit;
-    w->pending_v = v_unit;
     return static_cast<int>(KVC_OK);
   });
 }
 
 int kvc_windowed_keep(kvc_windowed_t* w, kvc_stream_t stream) {
+  (void)stream;  // the append already placed the unit's K/V in the ring's free slot
   return guarded("kvc_windowed_keep", [&] {
     if (!w) return fail(KVC_ERR_INVALID_ARGUMENT, "NULL handle");
     if (!w->pending) return fail(KVC_ERR_INVALID_ARGUMENT, "nothing appended");
-    if (w->overlap > 0 && w->k_ring) {
-      const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-      const size_t off = static_cast<size_t>(w->ring_head) * w->unit_bytes;
-      hipError_t e = hipMemcpyAsync(w->k_ring + off, w->pending_k, w->unit_bytes, hipMemcpyDeviceToDevice, st);
-      if (e == hipSuccess)
-        e = hipMemcpyAsync(w->v_ring + off, w->pending_v, w->unit_bytes, hipMemcpyDeviceToDevice, st);
-      if (e != hipSuccess) return fail(KVC_ERR_DEVICE, "ring copy: %s", hipGetErrorString(e));
-    }
     if (w->overlap > 0) {
-      w->ring_head = (w->ring_head + 1) % w->overlap;
+      // the slot written by the append now holds the newest kept unit; the
+      // next free slot held the unit kept overlap + 1 keeps ago
+      w->ring_head = (w->ring_head + 1) % ring_slots(w);
       w->ring_len = std::min(w->ring_len + 1, w->overlap);
     }
     ++w->slots;

@@ -29,7 +29,7 @@ class WindowedStream:
         L.check(lib.kvc_windowed_ring_bytes(cache.handle, overlap, C.byref(nb)), "kvc_windowed_ring_bytes")
         if nb.value:
             import torch
-            shp = (overlap, cache.unit_tokens, cache.num_heads, cache.head_dim)
+            shp = (overlap + 1, cache.unit_tokens, cache.num_heads, cache.head_dim)  # shared units + a free slot
             dt = torch_dtype(cache.dtype)
             self._ring = tuple(torch.empty(shp, dtype=dt, device=cache.k_pool.device) for _ in range(2))
             assert self._ring[0].numel() * self._ring[0].element_size() == nb.value
@@ -82,7 +82,8 @@ class WindowedStream:
         return bool(r.value)
 
     def keep(self, stream: Optional[int] = None) -> None:
-        """The last unit is a keyframe: it stays, takes one slot and enters the overlap ring."""
+        """The last unit is a keyframe: it stays, takes one slot, and its ring slot (written by the append)
+        becomes one of the shared units."""
         s = None
         if self.cache.device is not None:
             s = current_stream_ptr(self.cache.k_pool.device) if stream is None else stream
