@@ -53,3 +53,58 @@ def test_windowed_stream_25000_frames():
     assert ws.windows == oc.windows and ws.windows > 90
     assert dc.state() == oc.cache.state()
     assert checks >= 10
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_windowed_ring_slots_and_restarts(dtype):
+    """Every page type: each kept unit's K/V sit bit for bit in its ring slot (written by the append
+    itself), and attention right after each restart matches the oracle (the shared units re-appended
+    from the ring)."""
+    import numpy as np
+    import torch
+    from paged_sliding_window_kv_amd import KvCache, WindowedStream
+    H, P, X, S, W, N = 2, 256, 6, 2, 4, 3
+    slots, overlap, frames = 7, 3, 120
+    act = "f32" if dtype == "f32" else "bf16"
+    log(f"windowed ring: {dtype} pages, {frames} frames, window {slots}, overlap {overlap}, interval {N}")
+    bank = [synth.frame_qkv(74, 0, i, P + X, H, 64, act) for i in range(5)]
+    dev_bank = [tuple(to_dev(x, act) for x in f) for f in bank]
+    oc = OracleWindowed(OracleCache(OracleConfig(num_heads=H, head_dim=64, patch_tokens=P, special_tokens=X,
+                                                 num_scale_units=S, window_units=W, max_units=slots + 1,
+                                                 store_dtype=dtype)), slots, overlap)
+    dc = KvCache(num_heads=H, dtype=dtype, patch_tokens=P, special_tokens=X, num_scale_units=S, window_units=W,
+                 max_units=slots + 1, device="cuda")
+    ws = WindowedStream(dc, slots, overlap)
+    kring, vring = ws._ring
+    assert kring.shape[0] == overlap + 1
+    keeps = restarts = 0
+    for t in range(frames):
+        b = (t * 2) % len(bank)
+        q, k, v = bank[b]
+        dq, dk, dv = dev_bank[b]
+        r1 = oc.append(k, v)
+        r2 = ws.append(dk, dv)
+        assert r1 == r2
+        if r2:
+            restarts += 1
+            o, lse = dc.attend(dq)
+            torch.cuda.synchronize()
+            gk, gv = oc.cache.gather()
+            if dtype == "fp8":  # gather gives the dequantised values
+                ro, rl = attention_f64(bits_f64(q), gk, gv)
+            else:
+                ro, rl = attention_f64(bits_f64(q), bits_f64(gk), bits_f64(gv))
+            check_attention(o, lse, ro, rl, act, f"{dtype} t={t} restart {ws.windows} Lk={gk.shape[1]}")
+        if is_keyframe(t, S, N):
+            oc.keep()
+            ws.keep()
+            keeps += 1
+            slot = (keeps - 1) % (overlap + 1)
+            torch.cuda.synchronize()
+            assert torch.equal(kring[slot], dk) and torch.equal(vring[slot], dv), (t, slot)
+        else:
+            oc.drop()
+            ws.drop()
+    assert restarts == ws.windows == oc.windows >= 3
+    assert dc.state() == oc.cache.state()
+    assert np.array_equal(dc.visible_table()[0], np.array(oc.cache.visible_table()[0]))
