@@ -161,6 +161,7 @@ class CallClock:
         self.kernel_s = 0.0
         self.call_s = 0.0
         self.calls = 0
+        self.kernel_each = []  # seconds, one per call
 
     def before(self, i: int) -> None:
         self.ev[i][0].record()
@@ -176,9 +177,14 @@ class CallClock:
         self.torch.cuda.synchronize()
         for i in range(n):
             _, k0, k1, e = self.ev[i]
-            self.kernel_s += k0.elapsed_time(k1) * 1e-3
+            k = k0.elapsed_time(k1) * 1e-3
+            self.kernel_s += k
+            self.kernel_each.append(k)
             self.call_s += k0.elapsed_time(e) * 1e-3
         self.calls += n
+
+    def median_kernel_us(self) -> float:
+        return float(np.median(self.kernel_each)) * 1e6 if self.kernel_each else float("nan")
 
 
 def run_probes() -> dict:
@@ -298,13 +304,18 @@ def run_chunked(args) -> dict:
 
     for i in range(warm):
         step(i)
+    # one event at each step boundary as well (a 50 ms step: negligible), for the median step
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        marks[i].record()
         step(warm + i, i * L)
+    marks[steps].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     clock.collect(L * steps)
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
     lk = W * T
     if kr < 1.0:
         # keys each layer attends: the subset keeps the same table positions every steady-state step
@@ -343,8 +354,11 @@ def run_chunked(args) -> dict:
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": kernel, "per_launch_flops": flops_call, "per_launch_bytes": bytes_call,
-                     "avg_kernel_us": k_us, "avg_call_us_with_merge": c_us, "calls": n,
+                     "avg_kernel_us": k_us, "median_kernel_us": clock.median_kernel_us(),
+                     "avg_call_us_with_merge": c_us, "calls": n,
                      "call_tflops_with_merge": flops_call / (c_us * 1e-6) / 1e12},
+        "step_ms": {"median": float(np.median(step_ms)), "min": min(step_ms), "max": max(step_ms), "steps": steps,
+                    "source": "HIP events at the step boundaries of the timed region"},
     }
     if not args.no_cpu_baseline:
         rows = args.cpu_rows
@@ -550,7 +564,8 @@ def run_stream(args, timed: int | None = None, cpu_sample: int | None = None) ->
             "frac": ach_gbs / PEAK_HBM_GBS, "traffic": None,
             "kernel": "attn_bf16_kernel (272-row tile)" if args.kv_dtype == "bf16" else "attn_bf16_kernel<FP8 pages>",
             "per_launch_bytes": byt / n, "per_launch_flops": flo / n,
-            "avg_kernel_us": k_us, "avg_call_us_with_merge": c_us, "calls": n,
+            "avg_kernel_us": k_us, "median_kernel_us": clock.median_kernel_us(),
+            "avg_call_us_with_merge": c_us, "calls": n,
             "kernel_tflops": flo / clock.kernel_s / 1e12,
             "call_gbs_with_merge": byt / clock.call_s / 1e9,
         },
@@ -665,7 +680,8 @@ def run_stream_batched(args) -> dict:
                    "streams": B, "layers": L, "frames": frames, "timed_frames": timed},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                      "traffic": None, "kernel": "attn_bf16_kernel (batched)", "per_launch_bytes": byt / n,
-                     "avg_kernel_us": clock.kernel_s / n * 1e6, "avg_call_us_with_merge": clock.call_s / n * 1e6,
+                     "avg_kernel_us": clock.kernel_s / n * 1e6, "median_kernel_us": clock.median_kernel_us(),
+                     "avg_call_us_with_merge": clock.call_s / n * 1e6,
                      "calls": n, "kernel_tflops": flo / clock.kernel_s / 1e12},
     }
     if not args.no_cpu_baseline and args.cpu_sample > 0:
@@ -808,6 +824,7 @@ def run_global(args) -> dict:
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "attn_wide_kernel (global)",
                      "per_launch_flops": fl_g / L, "avg_kernel_us": kg * 1e6,
+                     "median_kernel_us": clock_g.median_kernel_us(),
                      "avg_call_us_with_merge": clock_g.call_s / clock_g.calls * 1e6, "calls": clock_g.calls,
                      "frame_attn_tflops": fl_f / L / tfr / 1e12},
     }
@@ -956,7 +973,7 @@ def run_keyframe(args) -> dict:
                    "device_memory_growth_bytes": mem1 - mem0},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_F32_TFLOPS, "traffic": None, "kernel": "attn_f32_kernel",
-                     "avg_kernel_us": clock.kernel_s / frames * 1e6,
+                     "avg_kernel_us": clock.kernel_s / frames * 1e6, "median_kernel_us": clock.median_kernel_us(),
                      "avg_call_us_with_merge": clock.call_s / frames * 1e6, "calls": frames},
     }
     if not args.no_cpu_baseline:
@@ -1183,6 +1200,7 @@ def run_windowed(args) -> dict:
         "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "attn_bf16_kernel (272-row tile)",
                      "per_launch_bytes": byt / n, "per_launch_flops": flo / n, "avg_kernel_us": k_us,
+                     "median_kernel_us": clock.median_kernel_us(),
                      "avg_call_us_with_merge": c_us, "calls": n, "replayed_frames": replay,
                      "kernel_tflops": flo / clock.kernel_s / 1e12},
     }
@@ -1396,6 +1414,8 @@ def main(argv=None):
     }
     if "cpu_baseline" in res:
         out["cpu_baseline"] = res["cpu_baseline"]
+    if "step_ms" in res:
+        out["step_ms"] = res["step_ms"]
     if extras:
         out["extras"] = extras
     if probes:
