@@ -36,3 +36,17 @@ def test_c_program_drives_a_host_only_cache(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("OK")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include/hip"),
+                    reason="needs gcc and the HIP headers")
+def test_device_program_compiles_as_c99(tmp_path):
+    """tests/c/abi_device.c (run on the GPU by tests/test_gpu_c_abi.py) builds as strict C99 against
+    libkvc.so and HIP's C API."""
+    L.lib()
+    libdir = os.path.dirname(os.path.abspath(L.LIB_PATH))
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+                        "-I/opt/rocm/include", os.path.join(ROOT, "tests", "c", "abi_device.c"),
+                        "-o", str(tmp_path / "abi_device"), f"-L{libdir}", "-lkvc", f"-Wl,-rpath,{libdir}",
+                        "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
