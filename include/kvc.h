@@ -452,7 +452,9 @@ int kvc_windowed_get_state(const kvc_windowed_t* w, kvc_windowed_state* out);
 
 const char* kvc_strerror(int status);
 const char* kvc_last_error(void);
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch.  300 (0.3.0): the
+ * windowed rings hold overlap + 1 units (kvc_windowed_ring_bytes), filled by
+ * the windowed append itself. */
 int kvc_version(void);
 
 /* Measurement hook for timing the attention kernel apart from the host-side

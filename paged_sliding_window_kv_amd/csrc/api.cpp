@@ -535,7 +535,7 @@ const char* kvc_strerror(int status) {
 
 const char* kvc_last_error(void) { return kvc::g_last_error; }
 
-int kvc_version(void) { return 200; }
+int kvc_version(void) { return 300; }
 
 int kvc_required_pages(const kvc_config* cfg, int32_t* num_pages) {
   return guarded("kvc_required_pages", [&] {

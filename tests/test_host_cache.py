@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.kvc_version() >= 200
+    assert lib.kvc_version() >= 300
 
 
 def _pair(**kw):
